@@ -1,0 +1,447 @@
+// qknorm_api.cpp -- the C ABI of libqknorm: argument validation, schedule
+// choice and launch. Validation runs entirely on the host and before any HIP
+// call, so every error path can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "qknorm.h"
+#include "qknorm_launch.h"
+
+struct qknorm_ctx {
+  int device;
+  int num_cus;
+  qknorm_options opt;
+};
+
+namespace {
+
+constexpr int64_t kVecBytes = 16;
+constexpr int kMaxSlices = 64;
+constexpr int kMaxSlots4 = 16;   // slots per lane, 4-wavefront workgroups
+constexpr int kMaxSlots16 = 8;   // slots per lane, 16-wavefront workgroups
+constexpr int64_t kMaxRows = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxTotalWidth = int64_t{1} << 24;  // exact as a float divisor
+
+int elem_bytes(int dtype) { return dtype == QKNORM_F32 ? 4 : 2; }
+int64_t vec_elems(int dtype) { return kVecBytes / elem_bytes(dtype); }
+bool valid_dtype(int dtype) { return dtype == QKNORM_F32 || dtype == QKNORM_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Byte footprint of `n` rows: row r starts at base + r*stride and is
+// `width` bytes long.
+struct Rows {
+  uintptr_t base;
+  int64_t width;
+  int64_t stride;
+  int64_t n;
+};
+
+// Do two row sets share a byte? Exact when their bounding ranges are apart,
+// or when they repeat with one period (the same stride, or one of them is a
+// single row) and their column windows are disjoint modulo that period, as
+// the query and key columns of one packed QKV buffer are. Otherwise
+// conservatively "yes".
+bool overlap(const Rows& a, const Rows& b) {
+  if (a.n <= 0 || b.n <= 0 || a.width <= 0 || b.width <= 0) return false;
+  const uintptr_t a_end = a.base + static_cast<uintptr_t>((a.n - 1) * a.stride + a.width);
+  const uintptr_t b_end = b.base + static_cast<uintptr_t>((b.n - 1) * b.stride + b.width);
+  if (a_end <= b.base || b_end <= a.base) return false;
+  int64_t S = 0;
+  if (a.n > 1 && b.n > 1)
+    S = a.stride == b.stride ? a.stride : 0;
+  else
+    S = a.n > 1 ? a.stride : b.stride;
+  if (S > 0 && a.width <= S && b.width <= S) {
+    int64_t d = static_cast<int64_t>(b.base - a.base) % S;
+    if (d < 0) d += S;
+    if (a.width <= d && d + b.width <= S) return false;
+  }
+  return true;
+}
+
+Rows in_rows(const qknorm_rows& r, int dtype, int64_t T) {
+  const int eb = elem_bytes(dtype);
+  return Rows{reinterpret_cast<uintptr_t>(r.x), r.width * eb, r.x_stride * eb, T};
+}
+Rows out_rows(const qknorm_rows& r, int dtype, int64_t T) {
+  const int eb = elem_bytes(dtype);
+  return Rows{reinterpret_cast<uintptr_t>(r.y), r.width * eb, r.y_stride * eb, T};
+}
+Rows flat(const void* p, int64_t bytes) {
+  return Rows{reinterpret_cast<uintptr_t>(p), bytes, bytes, 1};
+}
+
+// One tensor's shape checks (null, shape, alignment), shared by all calls.
+int check_rows(const qknorm_rows* r, const void* gamma, int dtype, bool need_y, bool need_gamma) {
+  if (r == nullptr || r->x == nullptr || (need_y && r->y == nullptr) ||
+      (need_gamma && gamma == nullptr))
+    return QKNORM_ERR_NULL;
+  if (r->width < 1 || r->x_stride < r->width || (need_y && r->y_stride < r->width))
+    return QKNORM_ERR_SHAPE;
+  const int64_t ve = vec_elems(dtype);
+  if (r->width % ve != 0 || r->x_stride % ve != 0 || (need_y && r->y_stride % ve != 0))
+    return QKNORM_ERR_ALIGN;
+  if (!aligned16(r->x) || (need_y && !aligned16(r->y)) || (need_gamma && !aligned16(gamma)))
+    return QKNORM_ERR_ALIGN;
+  return QKNORM_OK;
+}
+
+// In place (same pointer, same stride) or disjoint.
+bool in_out_ok(const qknorm_rows& r, int dtype, int64_t T) {
+  if (r.y == r.x) return r.y_stride == r.x_stride;
+  return !overlap(in_rows(r, dtype, T), out_rows(r, dtype, T));
+}
+
+bool eps_ok(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
+
+int check_ctx(const qknorm_ctx* ctx) {
+  if (ctx == nullptr) return QKNORM_ERR_CONTEXT;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device) return QKNORM_ERR_DEVICE;
+  return QKNORM_OK;
+}
+
+// How one segment's rows are spread over lanes.
+struct Plan {
+  int wpr_log2 = 0;
+  int slots = 0;
+  bool masked = false;
+};
+
+// Slots per lane with teams of 2^wl wavefronts: segmented and masked layouts.
+int seg_slots(int64_t slice_vec, int K, int wl) {
+  return static_cast<int>(K * ceil_div(slice_vec, int64_t{64} << wl));
+}
+int plain_slots(int64_t nvec, int wl) {
+  return static_cast<int>(ceil_div(nvec, int64_t{64} << wl));
+}
+
+// Choose the team size for one segment by its row width. The smallest team
+// whose slice layout fits the register budget wins: narrow rows get one
+// wavefront per row (several rows per workgroup, no LDS, no barrier), wide
+// rows get several wavefronts per row. `max_wl` is 2 for 4-wavefront
+// workgroups and 4 for 16-wavefront ones; `forced_wl` >= 0 pins the team.
+bool plan_segment(int64_t nvec, int K, int max_wl, int cap, int forced_wl, Plan* out) {
+  const int64_t slice_vec = nvec / K;
+  const int lo = forced_wl >= 0 ? forced_wl : 0;
+  const int hi = forced_wl >= 0 ? forced_wl : max_wl;
+  for (int wl = lo; wl <= hi; ++wl) {
+    const int n = seg_slots(slice_vec, K, wl);
+    if (n <= cap) {
+      *out = Plan{wl, n, false};
+      return true;
+    }
+  }
+  for (int wl = lo; wl <= hi; ++wl) {
+    const int n = plain_slots(nvec, wl);
+    if (n <= cap) {
+      *out = Plan{wl, n, true};
+      return true;
+    }
+  }
+  return false;
+}
+
+int forced_log2(const qknorm_ctx* ctx) {
+  switch (ctx->opt.waves_per_row) {
+    case 1: return 0;
+    case 2: return 1;
+    case 4: return 2;
+    case 8: return 3;
+    case 16: return 4;
+    default: return -1;
+  }
+}
+
+struct SegIn {
+  int64_t nvec;
+  int K;
+};
+
+// Plans a launch of 1 or 2 segments. Returns QKNORM_OK or QKNORM_ERR_SHAPE.
+int plan_launch(const qknorm_ctx* ctx, const SegIn* in, int nseg, Plan* plans, int* nw) {
+  const int fl = forced_log2(ctx);
+  bool ok = true;
+  bool wide = fl > 2;
+  if (!wide) {
+    for (int i = 0; i < nseg && ok; ++i) ok = plan_segment(in[i].nvec, in[i].K, 2, kMaxSlots4, fl, &plans[i]);
+    if (!ok) wide = fl < 0;  // retry with 16-wavefront workgroups
+  }
+  if (wide) {
+    ok = true;
+    for (int i = 0; i < nseg && ok; ++i) ok = plan_segment(in[i].nvec, in[i].K, 4, kMaxSlots16, fl, &plans[i]);
+    *nw = 16;
+  } else {
+    *nw = 4;
+  }
+  return ok ? QKNORM_OK : QKNORM_ERR_SHAPE;
+}
+
+// Lay one segment's rows out over the team's lanes (see qknorm_launch.h).
+// Segmented: each slice's vectors are dealt to the team from lane 0 again, so
+// every slot lies in one slice; masked: plain strided slots.
+void fill_layout(qkn::Seg* s, int wl, bool masked, int nw, int64_t nvec, int K, int64_t T) {
+  const int64_t nt = int64_t{64} << wl;
+  const int64_t slice_vec = nvec / K;
+  s->wpr_log2 = wl;
+  s->rows_per_wg = nw >> wl;
+  s->nwg = static_cast<int32_t>(ceil_div(T, s->rows_per_wg));
+  s->lay_k = K;
+  s->row_bytes = static_cast<uint32_t>(nvec * kVecBytes);
+  s->slice_vec = static_cast<int32_t>(slice_vec);
+  s->inv_slice_vec = 1.0f / static_cast<float>(slice_vec);
+  s->flush_mask = 0;
+  for (int j = 0; j < qkn::kMaxSlots; ++j) {
+    s->slot_base[j] = 0;
+    s->slot_lim[j] = 0;
+  }
+  if (masked) {
+    s->nslot = static_cast<int32_t>(ceil_div(nvec, nt));
+    for (int j = 0; j < s->nslot; ++j) {
+      s->slot_base[j] = static_cast<int32_t>(j * nt);
+      s->slot_lim[j] = static_cast<int32_t>(nvec - j * nt < nt ? nvec - j * nt : nt);
+    }
+    return;
+  }
+  const int64_t sps = ceil_div(slice_vec, nt);
+  s->nslot = static_cast<int32_t>(K * sps);
+  for (int j = 0; j < s->nslot; ++j) {
+    const int64_t sj = j / sps, ij = j % sps;
+    const int64_t left = slice_vec - ij * nt;
+    s->slot_base[j] = static_cast<int32_t>(sj * slice_vec + ij * nt);
+    s->slot_lim[j] = static_cast<int32_t>(left < nt ? left : nt);
+    if (ij == sps - 1) s->flush_mask |= 1u << j;
+  }
+}
+
+int grid_for(const qknorm_ctx* ctx, int64_t total_wg) {
+  int64_t g = total_wg;
+  if (ctx->opt.max_workgroups > 0 && g > ctx->opt.max_workgroups) g = ctx->opt.max_workgroups;
+  return static_cast<int>(g);
+}
+
+int run(const qkn::Variant& v, const qkn::Args& a, int grid, void* stream) {
+  if (grid <= 0) return QKNORM_OK;
+  const hipError_t e = qkn::launch(v, a, grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QKNORM_OK : QKNORM_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qknorm_status_string(int status) {
+  switch (status) {
+    case QKNORM_OK: return "ok";
+    case QKNORM_ERR_NULL: return "a required pointer is NULL";
+    case QKNORM_ERR_SHAPE: return "invalid shape: T, width, stride or h_total out of range";
+    case QKNORM_ERR_SLICES: return "invalid slicing: num_slices outside [1, 64], width not cut evenly "
+                                   "into whole 16-byte vectors, or slice_index out of range";
+    case QKNORM_ERR_ALIGN: return "pointer not 16-byte aligned, or width/stride not whole 16-byte vectors";
+    case QKNORM_ERR_DTYPE: return "unsupported dtype";
+    case QKNORM_ERR_EPS: return "eps must be finite and >= 0";
+    case QKNORM_ERR_ALIAS: return "an output overlaps an input without being that same input";
+    case QKNORM_ERR_DEVICE: return "no usable gfx950 device, wrong current device, or a HIP call failed";
+    case QKNORM_ERR_CONTEXT: return "context is NULL";
+    default: return "unknown status";
+  }
+}
+
+int64_t qknorm_max_width(int dtype) {
+  if (!valid_dtype(dtype)) return 0;
+  return int64_t{64} * 16 * kMaxSlots16 * vec_elems(dtype);
+}
+
+int qknorm_create_ex(qknorm_ctx** ctx_out, int device, const qknorm_options* opts) {
+  if (ctx_out == nullptr) return QKNORM_ERR_NULL;
+  *ctx_out = nullptr;
+  qknorm_options o{0, 0, 0};
+  if (opts != nullptr) {
+    o = *opts;
+    const int w = o.waves_per_row;
+    if (!(w == 0 || w == 1 || w == 2 || w == 4 || w == 8 || w == 16) || o.max_workgroups < 0 ||
+        (o.nontemporal != 0 && o.nontemporal != 1))
+      return QKNORM_ERR_SHAPE;
+  }
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return QKNORM_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return QKNORM_ERR_DEVICE;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return QKNORM_ERR_DEVICE;
+  qknorm_ctx* c = new (std::nothrow) qknorm_ctx{device, prop.multiProcessorCount, o};
+  if (c == nullptr) return QKNORM_ERR_DEVICE;
+  *ctx_out = c;
+  return QKNORM_OK;
+}
+
+int qknorm_create(qknorm_ctx** ctx_out, int device) { return qknorm_create_ex(ctx_out, device, nullptr); }
+
+int qknorm_destroy(qknorm_ctx* ctx) {
+  delete ctx;
+  return QKNORM_OK;
+}
+
+int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, const qknorm_rows* k,
+                   const void* gamma_q, const void* gamma_k, float eps, int num_slices, void* stream) {
+  if (!valid_dtype(dtype)) return QKNORM_ERR_DTYPE;
+  if (T < 0 || T > kMaxRows) return QKNORM_ERR_SHAPE;
+  if (T == 0) return QKNORM_OK;
+  const qknorm_rows* segs[2] = {q, k};
+  const void* gammas[2] = {gamma_q, gamma_k};
+  const int nseg = k != nullptr ? 2 : 1;
+  const int64_t ve = vec_elems(dtype);
+  for (int i = 0; i < nseg; ++i) {
+    const int st = check_rows(segs[i], gammas[i], dtype, true, true);
+    if (st != QKNORM_OK) return st;
+    if (segs[i]->width > qknorm_max_width(dtype)) return QKNORM_ERR_SHAPE;
+    if (num_slices < 1 || num_slices > kMaxSlices || segs[i]->width % num_slices != 0 ||
+        (segs[i]->width / num_slices) % ve != 0)
+      return QKNORM_ERR_SLICES;
+  }
+  if (!eps_ok(eps)) return QKNORM_ERR_EPS;
+  const int eb = elem_bytes(dtype);
+  for (int i = 0; i < nseg; ++i) {
+    if (!in_out_ok(*segs[i], dtype, T)) return QKNORM_ERR_ALIAS;
+    const Rows yi = out_rows(*segs[i], dtype, T);
+    for (int j = 0; j < nseg; ++j) {
+      if (overlap(yi, flat(gammas[j], segs[j]->width * eb))) return QKNORM_ERR_ALIAS;
+      if (j == i) continue;
+      if (overlap(yi, in_rows(*segs[j], dtype, T)) || overlap(yi, out_rows(*segs[j], dtype, T)))
+        return QKNORM_ERR_ALIAS;
+    }
+  }
+  int st = check_ctx(ctx);
+  if (st != QKNORM_OK) return st;
+
+  SegIn in[2];
+  for (int i = 0; i < nseg; ++i) in[i] = SegIn{segs[i]->width / ve, num_slices};
+  Plan plans[2];
+  int nw = 4;
+  st = plan_launch(ctx, in, nseg, plans, &nw);
+  if (st != QKNORM_OK) return st;
+
+  bool masked = false;
+  for (int i = 0; i < nseg; ++i) masked = masked || plans[i].masked;
+  qkn::Args a{};
+  a.T = T;
+  a.nseg = nseg;
+  a.eps = eps;
+  int slots = 0;
+  int64_t total = 0;
+  for (int i = 0; i < nseg; ++i) {
+    qkn::Seg& s = a.seg[i];
+    s.x = segs[i]->x;
+    s.y = segs[i]->y;
+    s.gamma = gammas[i];
+    s.x_stride = segs[i]->x_stride;
+    s.y_stride = segs[i]->y_stride;
+    // one kernel serves both segments, so a masked plan for either puts both
+    // in the masked layout (never more slots than their segmented plan)
+    fill_layout(&s, plans[i].wpr_log2, masked, nw, in[i].nvec, num_slices, T);
+    s.h = static_cast<float>(segs[i]->width);
+    s.comb_k = 0;
+    slots = s.nslot > slots ? s.nslot : slots;
+    total += s.nwg;
+  }
+  if (total > kMaxRows) return QKNORM_ERR_SHAPE;
+  a.total_wg = static_cast<int32_t>(total);
+  qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw), nw, masked,
+                 ctx->opt.nontemporal == 1 && !masked};
+  if (v.vpl == 0) return QKNORM_ERR_SHAPE;
+  return run(v, a, grid_for(ctx, total), stream);
+}
+
+int qknorm_partial_stats(qknorm_ctx* ctx, int dtype, int64_t T, const void* x_slice, int64_t x_stride,
+                         int64_t slice_width, int slice_index, int num_slices, float* stats, void* stream) {
+  if (!valid_dtype(dtype)) return QKNORM_ERR_DTYPE;
+  if (T < 0 || T > kMaxRows) return QKNORM_ERR_SHAPE;
+  if (T == 0) return QKNORM_OK;
+  if (x_slice == nullptr || stats == nullptr) return QKNORM_ERR_NULL;
+  const qknorm_rows r{x_slice, nullptr, slice_width, x_stride, slice_width};
+  int st = check_rows(&r, nullptr, dtype, false, false);
+  if (st != QKNORM_OK) return st;
+  if (slice_width > qknorm_max_width(dtype)) return QKNORM_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(stats) & 3u) != 0) return QKNORM_ERR_ALIGN;
+  if (num_slices < 1 || num_slices > kMaxSlices || slice_index < 0 || slice_index >= num_slices)
+    return QKNORM_ERR_SLICES;
+  float* out = stats + static_cast<int64_t>(slice_index) * T;
+  if (overlap(flat(out, T * 4), in_rows(r, dtype, T))) return QKNORM_ERR_ALIAS;
+  st = check_ctx(ctx);
+  if (st != QKNORM_OK) return st;
+
+  const int64_t nvec = slice_width / vec_elems(dtype);
+  const SegIn in{nvec, 1};
+  Plan plan;
+  int nw = 4;
+  st = plan_launch(ctx, &in, 1, &plan, &nw);
+  if (st != QKNORM_OK) return st;
+  qkn::Args a{};
+  a.T = T;
+  a.nseg = 1;
+  a.eps = 0.0f;
+  qkn::Seg& s = a.seg[0];
+  s.x = x_slice;
+  s.x_stride = x_stride;
+  s.stats_out = out;
+  fill_layout(&s, plan.wpr_log2, false, nw, nvec, 1, T);
+  s.h = static_cast<float>(slice_width);
+  a.total_wg = s.nwg;
+  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(s.nslot, nw), nw, false, false};
+  if (v.vpl == 0) return QKNORM_ERR_SHAPE;
+  return run(v, a, grid_for(ctx, s.nwg), stream);
+}
+
+int qknorm_apply_stats(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* x_slice,
+                       const void* gamma_slice, const float* stats, int num_slices, int64_t h_total,
+                       float eps, void* stream) {
+  if (!valid_dtype(dtype)) return QKNORM_ERR_DTYPE;
+  if (T < 0 || T > kMaxRows) return QKNORM_ERR_SHAPE;
+  if (T == 0) return QKNORM_OK;
+  if (stats == nullptr) return QKNORM_ERR_NULL;
+  int st = check_rows(x_slice, gamma_slice, dtype, true, true);
+  if (st != QKNORM_OK) return st;
+  if (x_slice->width > qknorm_max_width(dtype) || h_total < x_slice->width || h_total > kMaxTotalWidth)
+    return QKNORM_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(stats) & 3u) != 0) return QKNORM_ERR_ALIGN;
+  if (num_slices < 1 || num_slices > kMaxSlices) return QKNORM_ERR_SLICES;
+  if (!eps_ok(eps)) return QKNORM_ERR_EPS;
+  const int eb = elem_bytes(dtype);
+  const Rows yr = out_rows(*x_slice, dtype, T);
+  if (!in_out_ok(*x_slice, dtype, T) || overlap(yr, flat(stats, num_slices * T * 4)) ||
+      overlap(yr, flat(gamma_slice, x_slice->width * eb)))
+    return QKNORM_ERR_ALIAS;
+  st = check_ctx(ctx);
+  if (st != QKNORM_OK) return st;
+
+  const int64_t nvec = x_slice->width / vec_elems(dtype);
+  const SegIn in{nvec, 1};
+  Plan plan;
+  int nw = 4;
+  st = plan_launch(ctx, &in, 1, &plan, &nw);
+  if (st != QKNORM_OK) return st;
+  qkn::Args a{};
+  a.T = T;
+  a.nseg = 1;
+  a.eps = eps;
+  qkn::Seg& s = a.seg[0];
+  s.x = x_slice->x;
+  s.y = x_slice->y;
+  s.gamma = gamma_slice;
+  s.stats_in = stats;
+  s.x_stride = x_slice->x_stride;
+  s.y_stride = x_slice->y_stride;
+  fill_layout(&s, plan.wpr_log2, false, nw, nvec, 1, T);
+  s.comb_k = num_slices;
+  s.h = static_cast<float>(h_total);
+  a.total_wg = s.nwg;
+  qkn::Variant v{dtype, qkn::MODE_APPLY, qkn::compiled_vpl(s.nslot, nw), nw, false, false};
+  if (v.vpl == 0) return QKNORM_ERR_SHAPE;
+  return run(v, a, grid_for(ctx, s.nwg), stream);
+}
+
+}  // extern "C"

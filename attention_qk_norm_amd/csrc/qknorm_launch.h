@@ -1,0 +1,83 @@
+// qknorm_launch.h -- what the host API hands to the gfx950 kernels.
+//
+// One launch covers up to two "segments": the query rows and the key rows of
+// the same tokens (or the single tensor of a split-path call). Each segment
+// is processed by teams of `wpr` wavefronts; a team owns one row at a time.
+//
+// Register layout of a row inside a team ("slots"): the row's 16-byte
+// vectors are grouped by column slice, and each slice's vectors are dealt to
+// the team's lanes starting again at lane 0 of the team. Slot j of a lane
+// therefore always lies inside one slice, and a slice's partial sum of squares
+// is a plain team-wide reduction over the slots of that slice. `sps` slots
+// cover one slice; a row needs `lay_k * sps` slots per lane. With one slice
+// this is the usual strided layout (vector v in lane v % team, slot v / team).
+//
+// When that would need too many slots (many slices narrower than the team),
+// the kernel falls back to the "masked" layout: plain strided vectors, and a
+// per-lane slice index selects which partial each vector's squares join.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkn {
+
+enum Mode : int {
+  MODE_FWD = 0,    // statistic and scaling in one pass (row stays in registers)
+  MODE_STATS = 1,  // statistic only: one fp32 per row to `stats_out`
+  MODE_APPLY = 2,  // combine `comb_k` precomputed partials, then scale
+};
+
+constexpr int kMaxSlots = 16;  // slots per lane of the widest compiled variant
+
+struct Seg {
+  const void* x;          // row 0 of the input
+  void* y;                // row 0 of the output (FWD, APPLY)
+  const void* gamma;      // weights of the columns processed (FWD, APPLY)
+  const float* stats_in;  // APPLY: partials laid out [comb_k][T]
+  float* stats_out;       // STATS: row t's sum goes to stats_out[t]
+  int64_t x_stride;       // elements between input rows
+  int64_t y_stride;       // elements between output rows
+  int32_t wpr_log2;       // log2 of the wavefronts per team
+  int32_t rows_per_wg;    // teams per workgroup
+  int32_t nwg;            // workgroups covering all T rows
+  int32_t nslot;          // slots per lane in use
+  uint32_t row_bytes;     // bytes of one row processed (and of its weights)
+  int32_t lay_k;          // partial sums per row (slices)
+  int32_t comb_k;         // APPLY: partials combined per row
+  int32_t slice_vec;      // masked layout: vectors per slice
+  float inv_slice_vec;    // masked layout: 1.0f / slice_vec
+  float h;                // the mean of squares divides by this width
+  uint32_t flush_mask;    // segmented layout: bit j set when slot j ends a slice
+  // Slot j of team lane `tl` holds vector slot_base[j] + tl of the row when
+  // tl < slot_lim[j], and nothing otherwise (slot_lim[j] = 0 for j >= nslot).
+  int32_t slot_base[kMaxSlots];
+  int32_t slot_lim[kMaxSlots];
+};
+
+struct Args {
+  Seg seg[2];
+  int64_t T;         // rows per segment
+  int32_t nseg;      // 1 or 2
+  int32_t total_wg;  // seg[0].nwg + seg[1].nwg (when nseg == 2)
+  float eps;
+};
+
+// Compile-time variants a launch picks from.
+struct Variant {
+  int dtype;     // qknorm_dtype
+  int mode;      // Mode
+  int vpl;       // slots per lane the kernel is built for (>= what the segments need)
+  int nw;        // wavefronts per workgroup: 4 or 16
+  bool masked;   // FWD only: masked layout
+  bool nt;       // FWD only: non-temporal row loads and stores
+};
+
+// Smallest compiled slot count >= `slots` for `nw` wavefronts per workgroup,
+// or 0 when none is large enough.
+int compiled_vpl(int slots, int nw);
+
+// Enqueue one launch of `grid` workgroups. Returns hipSuccess or the launch error.
+hipError_t launch(const Variant& v, const Args& a, int grid, hipStream_t stream);
+
+}  // namespace qkn

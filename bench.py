@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the fused layerwise QK-Norm forward on one MI355X.
+
+One step = one fused forward (statistic, slice combine, scaling, store) over
+the query rows and key rows of one batch of T tokens, inputs resident in HBM.
+The default workload is the large-prefill configuration (T = 16384, query and
+key rows of 4096 bf16, Laplace(0, 1) values, 8 column slices, in-place
+output), the one measured against the HBM roofline. Buffer sets are rotated
+so that no launch finds its data in the 256 MB Infinity Cache.
+
+Prints one JSON line. Kernel time comes from HIP events recorded around
+every launch on the stream the kernel runs on (torch's current stream).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QK-Norm tokens/sec and achieved HBM GB/s (% of peak) at 1 MI355X"
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+CPU_SHARE = 16         # host cores per GPU on the measurement boxes
+KERNEL_SOURCES = ("attention_qk_norm_amd/csrc/qknorm_kernels.hip",
+                  "attention_qk_norm_amd/csrc/qknorm_api.cpp",
+                  "attention_qk_norm_amd/csrc/qknorm_launch.h")
+TRAFFIC_FILE = "profiles/qknorm_fwd_{workload}_traffic.json"
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"])
+    p.add_argument("--num-slices", type=int, default=None,
+                   help="slices of the row statistic (default: the workload's primary count)")
+    p.add_argument("--rotate-mib", type=int, default=2048,
+                   help="total size of the rotated buffer sets")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time spent timing the oracle")
+    p.add_argument("--waves-per-row", type=int, default=0)
+    p.add_argument("--max-workgroups", type=int, default=0)
+    p.add_argument("--nontemporal", type=int, default=0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also launch a plain elementwise copy of known size (counter calibration)")
+    p.add_argument("--quiet", action="store_true")
+    return p.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(d, num_slices, seconds):
+    """The fp64 oracle, as it is, on a bounded sample of the workload's rows."""
+    import numpy as np
+    import oracle
+    cores = min(CPU_SHARE, os.cpu_count() or 1)
+    oracle.set_threads(cores)
+    w = d["w"]
+    # sample: the first `rows` tokens of q and k; grow until one pass is >= 0.5 s
+    rows = min(w.T, 256)
+    qs = oracle.as_f32(d["q"])
+    ks = oracle.as_f32(d["k"])
+    gq, gk = oracle.as_f32(d["gamma_q"]), oracle.as_f32(d["gamma_k"])
+    while True:
+        t0 = time.perf_counter()
+        oracle.qk_forward(qs[:rows], ks[:rows], gq, gk, w.eps, num_slices)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 or rows >= w.T:
+            break
+        rows = min(w.T, rows * 2)
+    reps = max(1, int(seconds / max(dt, 1e-6)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.qk_forward(qs[:rows], ks[:rows], gq, gk, w.eps, num_slices)
+    total = time.perf_counter() - t0
+    oracle.set_threads(1)
+    return {"value": rows * reps / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d tokens (q %d + k %d columns, %s), K=%d, %d passes in %.1f s" % (
+                rows, w.T, w.hq, w.hk, w.dtype, num_slices, reps, total)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_qk_norm_amd as qk
+    from attention_qk_norm_amd import workloads
+
+    if not os.path.exists(qk.LIB_PATH):
+        from attention_qk_norm_amd import build as qbuild
+        qbuild.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    d = workloads.generate(args.workload)
+    w = d["w"]
+    K = args.num_slices or w.slices[0]
+    eb = w.elem_bytes
+    algo_bytes = w.algorithmic_bytes()
+    log(args, "workload %s (%s): T=%d Hq=%d Hk=%d %s K=%d in_place=%s, %.1f MB per call" % (
+        args.workload, w.name, w.T, w.hq, w.hk, w.dtype, K, w.in_place, algo_bytes / 1e6))
+
+    # buffer sets, rotated so consecutive launches touch different memory
+    set_bytes = w.T * (w.hq + w.hk) * eb * (1 if w.in_place else 2)
+    nsets = max(2, math.ceil(args.rotate_mib * 2**20 / set_bytes))
+    q0, k0 = d["q"].to(dev), d["k"].to(dev)
+    gq, gk = d["gamma_q"].to(dev), d["gamma_k"].to(dev)
+    sets = []
+    for _ in range(nsets):
+        q, k = q0.clone(), k0.clone()
+        if w.in_place:
+            sets.append((q, k, q, k))
+        else:
+            sets.append((q, k, torch.empty_like(q), torch.empty_like(k)))
+    del q0, k0
+    log(args, "%d buffer sets, %.0f MiB" % (nsets, nsets * set_bytes / 2**20))
+
+    ctx = qk.Context(0, waves_per_row=args.waves_per_row, max_workgroups=args.max_workgroups,
+                     nontemporal=args.nontemporal)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, num_slices=K):
+        q, k, yq, yk = sets[i % nsets]
+        qk.forward(q, k, gq, gk, eps=w.eps, num_slices=num_slices, out_q=yq, out_k=yk, ctx=ctx,
+                   stream=stream)
+
+    calib = None
+    if args.calibrate_copy:
+        n = 64 * 2**20  # elements of fp32: 256 MiB read + 256 MiB written
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        calib = {"kernel": "torch.neg fp32", "read_bytes": 4 * n, "write_bytes": 4 * n}
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K launches, an event pair around each
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    region0, region1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    region0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    region_ms = region0.elapsed_time(region1)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    kern_ms_mean = sum(per) / len(per)
+    kern_ms_p50 = per[len(per) // 2]
+    ms_per_step = region_ms / args.steps
+
+    # back-to-back launches without per-launch events (throughput as a caller sees it)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    b2b_ms = b0.elapsed_time(b1) / args.steps
+
+    # the other slicing of the same workload, and a same-bytes device copy
+    extra = {}
+    for k_alt in w.slices:
+        if k_alt == K:
+            continue
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(args.warmup):
+            step(i, k_alt)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(i, k_alt)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        extra["ms_per_step_K%d" % k_alt] = e0.elapsed_time(e1) / args.steps
+    nb = w.T * (w.hq + w.hk) * eb
+    csets = max(2, math.ceil(args.rotate_mib * 2**20 / (2 * nb)))
+    cbufs = [(torch.empty(nb, dtype=torch.uint8, device=dev), torch.empty(nb, dtype=torch.uint8, device=dev))
+             for _ in range(csets)]
+    for s, t in cbufs:
+        t.copy_(s)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(args.steps):
+        s, t = cbufs[i % csets]
+        t.copy_(s)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / args.steps
+    del cbufs
+
+    achieved_gbs = algo_bytes / (kern_ms_mean * 1e-3) / 1e9
+    traffic = None
+    tf = os.path.join(ROOT, TRAFFIC_FILE.format(workload=args.workload))
+    if os.path.exists(tf):
+        with open(tf) as f:
+            t = json.load(f)
+        if t.get("kernel_source_sha") == kernel_source_sha() and t.get("num_slices") == K:
+            traffic = t.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": w.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s %s: T=%d, q rows %d, k rows %d, %s in/out, %s values, K=%d slices%s" % (
+            args.workload, w.name, w.T, w.hq, w.hk, w.dtype, w.dist, K, ", in place" if w.in_place else ""),
+            "tokens": w.T, "q_width": w.hq, "k_width": w.hk, "io_dtype": w.dtype, "num_slices": K,
+            "in_place": w.in_place, "buffer_sets": nsets, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic},
+        "hbm_gbs": achieved_gbs,
+        "algorithmic_bytes_per_launch": algo_bytes,
+        "kernel_us_mean": kern_ms_mean * 1e3,
+        "kernel_us_p50": kern_ms_p50 * 1e3,
+        "back_to_back_us": b2b_ms * 1e3,
+        "copy_same_bytes_us": copy_ms * 1e3,
+        "copy_same_bytes_gbs": 2 * nb / (copy_ms * 1e-3) / 1e9,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    result.update({k2: v for k2, v in extra.items()})
+    if calib:
+        result["calibration_copy"] = calib
+    if not args.no_cpu_baseline:
+        log(args, "timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(d, K, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

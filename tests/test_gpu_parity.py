@@ -1,0 +1,308 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Every case prints what it runs before the GPU call so a failing run names it.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import attention_qk_norm_amd as qk
+import oracle
+from attention_qk_norm_amd import workloads
+from conftest import read_golden
+from gpu_checks import assert_near_each_other, assert_parity, host64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _oracle_threads():
+    oracle.set_threads(min(16, os.cpu_count() or 1))
+    yield
+    oracle.set_threads(1)
+
+
+def gpu(t):
+    return t.to(DEV).contiguous()
+
+
+def run_forward(q, k, gq, gk, eps, K, in_place=False, ctx=None):
+    qd, kd = gpu(q), (gpu(k) if k is not None else None)
+    out_q = qd if in_place else None
+    out_k = kd if (in_place and kd is not None) else None
+    yq, yk = qk.forward(qd, kd, gpu(gq), gpu(gk) if gk is not None else None, eps=eps, num_slices=K,
+                        out_q=out_q, out_k=out_k, ctx=ctx)
+    torch.cuda.synchronize()
+    return yq, yk
+
+
+# ---- the five workloads at full size ------------------------------------------
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_workload_parity(name):
+    d = workloads.generate(name)
+    w = d["w"]
+    refs = {}
+    outs = {}
+    for K in w.slices:
+        say(name, w.name, "T=%d Hq=%d Hk=%d %s K=%d in_place=%s" % (w.T, w.hq, w.hk, w.dtype, K, w.in_place))
+        yq, yk = run_forward(d["q"], d["k"], d["gamma_q"], d["gamma_k"], w.eps, K, in_place=w.in_place)
+        if not refs:
+            refs["q"], _ = oracle.forward(d["q"], d["gamma_q"], w.eps, K)
+            refs["k"], _ = oracle.forward(d["k"], d["gamma_k"], w.eps, K)
+        eq = assert_parity(yq, refs["q"], w.torch_dtype, "%s q K=%d" % (name, K))
+        ek = assert_parity(yk, refs["k"], w.torch_dtype, "%s k K=%d" % (name, K))
+        print("  q errors", eq, "\n  k errors", ek, flush=True)
+        outs[K] = (yq.cpu(), yk.cpu())
+        del yq, yk
+    # the K-slice statistic reaches the same outputs as one slice up to rounding
+    if len(outs) > 1:
+        (a_q, a_k), (b_q, b_k) = list(outs.values())[:2]
+        for a, b in ((a_q, b_q), (a_k, b_k)):
+            same = assert_near_each_other(a, b, w.torch_dtype, name + " K vs 1")
+            print("  K=%d vs K=%d: %.4f of elements bitwise equal" % (w.slices[0], w.slices[1], same),
+                  flush=True)
+
+
+# ---- pins that hold on the GPU too ------------------------------------------------
+
+def test_worked_example_on_gpu():
+    """SwiftQK review section 4b, Eqs. (2)-(8), in fp32: fused with K = 2 and
+    K = 1, and the per-shard split path."""
+    g = read_golden("swiftqk_worked_example.txt")
+    x = torch.tensor([g["x"]], dtype=torch.float32)
+    gam = torch.tensor(g["gamma"], dtype=torch.float32)
+    eps = g["eps"][0]
+    ref, _ = oracle.forward(x, gam, eps, 2)
+    for K in (2, 1):
+        say("worked example fp32 K=%d" % K)
+        yq, _ = run_forward(x, None, gam, None, eps, K)
+        assert_parity(yq, ref, torch.float32, "worked example K=%d" % K)
+        y = host64(yq)[0]
+        for j in range(8):
+            assert abs(y[j] - g["y"][j]) <= 0.5e-3 + abs(g["x"][j]) * 0.5e-4, (j, y[j])
+    say("worked example split path")
+    xd = gpu(x)
+    stats = torch.zeros((2, 1), dtype=torch.float32, device=DEV)
+    for r in range(2):
+        qk.partial_stats(xd[:, 4 * r:4 * r + 4], r, 2, stats)
+    torch.cuda.synchronize()
+    assert stats.cpu().flatten().tolist() == g["S_local"]  # Eqs. 3-4, exact
+    for r in range(2):
+        yr = qk.apply_stats(xd[:, 4 * r:4 * r + 4], gpu(gam[4 * r:4 * r + 4]), stats, 8, eps)
+        torch.cuda.synchronize()
+        assert_parity(yr, ref[:, 4 * r:4 * r + 4], torch.float32, "Eq. %d" % (7 + r))
+
+
+def test_four_element_closed_form_on_gpu():
+    x = torch.tensor([[1.0, 2.0, -1.0, 0.5]])
+    say("four-element closed form")
+    y, _ = run_forward(x, None, torch.ones(4), None, 0.0, 1)
+    assert_parity(y, np.array([[0.8, 1.6, -0.8, 0.4]]), torch.float32, "eps=0")
+    y, _ = run_forward(x, None, torch.tensor([1.0, 0.5, 2.0, 4.0]), None, 0.0, 1)
+    assert_parity(y, np.array([[0.8, 0.8, -1.6, 1.6]]), torch.float32, "gamma")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_exact_sums_bitwise_across_slicings(dtype):
+    """On n/16 inputs every partial is exact in fp32, so the statistic is the
+    same whatever the slicing: K-slice outputs are bitwise those of K = 1, and
+    the split path's partials equal the exact integer sums."""
+    T, H = 37, 4096
+    x = workloads.exact_sum_rows(T, H, dtype, 71)
+    k = workloads.exact_sum_rows(T, 1024, dtype, 72)
+    gq = workloads.random_weights(H, dtype, 73)
+    gk = workloads.random_weights(1024, dtype, 74)
+    n = np.rint(host64(x) * 16).astype(np.int64)
+    base = None
+    for K in (1, 2, 4, 8, 16, 32, 64):
+        say("exact sums", dtype, "K=%d" % K)
+        yq, yk = run_forward(x, k, gq, gk, 1e-6, K)
+        if base is None:
+            base = (yq.cpu(), yk.cpu())
+            ref, _ = oracle.forward(x, gq, 1e-6, 1)
+            assert_parity(yq, ref, workloads.DTYPES[dtype], "exact-sum forward")
+        else:
+            assert torch.equal(yq.cpu(), base[0]), K
+            assert torch.equal(yk.cpu(), base[1]), K
+        w = H // K
+        xd = gpu(x)
+        stats = torch.zeros((K, T), dtype=torch.float32, device=DEV)
+        for s in range(K):
+            qk.partial_stats(xd[:, s * w:(s + 1) * w], s, K, stats)
+        torch.cuda.synchronize()
+        ns = n.reshape(T, K, w)
+        want = (ns * ns).sum(axis=2).T / 256.0
+        assert np.array_equal(stats.cpu().numpy().astype(np.float64), want), K
+
+
+# ---- split path -------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_split_path_matches_oracle(name):
+    """partial_stats for every slice, then apply_stats per slice (the
+    single-GPU analogue of scalar aggregation across tensor-parallel ranks)."""
+    d = workloads.generate(name)
+    w = d["w"]
+    K = w.slices[0]
+    T = min(w.T, 2048)
+    for which in ("q", "k"):
+        x, g = d[which][:T], d["gamma_" + which]
+        H = x.shape[1]
+        wd = H // K
+        say("split path", name, which, "T=%d H=%d K=%d" % (T, H, K))
+        ref, Pref = oracle.forward(x, g, w.eps, K)
+        xd, gd = gpu(x), gpu(g)
+        stats = torch.zeros((K, T), dtype=torch.float32, device=DEV)
+        for s in range(K):
+            qk.partial_stats(xd[:, s * wd:(s + 1) * wd], s, K, stats)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(stats.cpu().numpy(), Pref, rtol=1e-5)
+        y = torch.empty_like(xd)
+        for s in range(K):
+            qk.apply_stats(xd[:, s * wd:(s + 1) * wd], gd[s * wd:(s + 1) * wd], stats, H, w.eps,
+                           out=y[:, s * wd:(s + 1) * wd])
+        torch.cuda.synchronize()
+        assert_parity(y, ref, w.torch_dtype, "split %s %s" % (name, which))
+        # in place, slice by slice
+        for s in range(K):
+            v = xd[:, s * wd:(s + 1) * wd]
+            qk.apply_stats(v, gd[s * wd:(s + 1) * wd], stats, H, w.eps, out=v)
+        torch.cuda.synchronize()
+        assert torch.equal(xd.cpu(), y.cpu())
+
+
+# ---- ragged shapes, strides, schedules ---------------------------------------------
+
+RAGGED = [
+    # (dtype, T, Hq, Hk, K)
+    ("bf16", 1, 8, 8, 1),
+    ("bf16", 3, 24, 16, 1),
+    ("bf16", 5, 1000, 200, 5),       # ragged last slot, slices of 200 / 40
+    ("bf16", 63, 1032, 520, 1),
+    ("bf16", 65, 5120, 1024, 4),     # C3/C4 widths, odd T
+    ("bf16", 7, 4096, 4096, 64),     # 64 slices of 64: masked layout
+    ("bf16", 9, 12288, 1536, 3),
+    ("bf16", 4, 16384, 16384, 8),    # wider than one wavefront's 16 slots
+    ("bf16", 3, 65536, 8, 1),        # widest accepted row, with a tiny key row
+    ("bf16", 2, 32768, 32768, 16),
+    ("f32", 1, 4, 4, 1),
+    ("f32", 6, 260, 12, 1),
+    ("f32", 33, 256, 256, 4),
+    ("f32", 17, 4096, 1024, 2),
+    ("f32", 3, 8192, 8192, 8),
+    ("f32", 2, 32768, 4, 1),         # widest fp32 row
+    ("f32", 5, 1536, 1536, 48),      # 48 slices of 32: masked layout
+]
+
+
+@pytest.mark.parametrize("dtype,T,Hq,Hk,K", RAGGED)
+def test_ragged_shapes(dtype, T, Hq, Hk, K):
+    q = workloads.random_rows(T, Hq, dtype, [T, Hq, 1], dist="laplace")
+    k = workloads.random_rows(T, Hk, dtype, [T, Hk, 2], scale=3.0)
+    gq = workloads.random_weights(Hq, dtype, [Hq, 3])
+    gk = workloads.random_weights(Hk, dtype, [Hk, 4])
+    say("ragged", dtype, T, Hq, Hk, K)
+    yq, yk = run_forward(q, k, gq, gk, 1e-6, K)
+    rq, _ = oracle.forward(q, gq, 1e-6, K)
+    rk, _ = oracle.forward(k, gk, 1e-6, K)
+    assert_parity(yq, rq, workloads.DTYPES[dtype], "q")
+    assert_parity(yk, rk, workloads.DTYPES[dtype], "k")
+
+
+@pytest.mark.parametrize("opts", [dict(waves_per_row=1), dict(waves_per_row=2), dict(waves_per_row=4),
+                                  dict(waves_per_row=8), dict(waves_per_row=16),
+                                  dict(max_workgroups=7), dict(max_workgroups=300, waves_per_row=2),
+                                  dict(nontemporal=1)],
+                         ids=lambda o: ",".join("%s=%s" % kv for kv in o.items()))
+def test_schedules_agree(opts):
+    """Every schedule (team size, persistent grid, streaming stores) computes
+    the same rows."""
+    ctx = qk.Context(0, **opts)
+    for dtype, T, Hq, Hk, K in (("bf16", 131, 5120, 1024, 4), ("f32", 45, 2048, 512, 2)):
+        q = workloads.random_rows(T, Hq, dtype, [7, T])
+        k = workloads.random_rows(T, Hk, dtype, [8, T])
+        gq = workloads.random_weights(Hq, dtype, 9)
+        gk = workloads.random_weights(Hk, dtype, 10)
+        say("schedule", opts, dtype, T, Hq, Hk, K)
+        try:
+            yq, yk = run_forward(q, k, gq, gk, 1e-6, K, ctx=ctx)
+        except qk.QKNormError as e:
+            # a pinned team too small for the row is refused on the host
+            assert e.status == qk.ERR_SHAPE and "waves_per_row" in opts
+            continue
+        rq, _ = oracle.forward(q, gq, 1e-6, K)
+        rk, _ = oracle.forward(k, gk, 1e-6, K)
+        assert_parity(yq, rq, workloads.DTYPES[dtype], "q")
+        assert_parity(yk, rk, workloads.DTYPES[dtype], "k")
+
+
+def test_strided_views_and_packed_qkv_in_place():
+    """q and k as column blocks of one packed [T, Hq + Hk + Hv] buffer,
+    normalised in place; the value columns and everything outside the views
+    must come back untouched."""
+    T, Hq, Hk, Hv = 77, 2048, 512, 512
+    H = Hq + Hk + Hv
+    qkv = workloads.random_rows(T, H, "bf16", 81)
+    gq = workloads.random_weights(Hq, "bf16", 82)
+    gk = workloads.random_weights(Hk, "bf16", 83)
+    rq, _ = oracle.forward(qkv[:, :Hq], gq, 1e-6, 1)
+    rk, _ = oracle.forward(qkv[:, Hq:Hq + Hk], gk, 1e-6, 1)
+    dev = gpu(qkv)
+    q, k = dev[:, :Hq], dev[:, Hq:Hq + Hk]
+    say("packed qkv in place")
+    qk.forward(q, k, gpu(gq), gpu(gk), eps=1e-6, out_q=q, out_k=k)
+    torch.cuda.synchronize()
+    out = dev.cpu()
+    assert_parity(out[:, :Hq], rq, torch.bfloat16, "q")
+    assert_parity(out[:, Hq:Hq + Hk], rk, torch.bfloat16, "k")
+    assert torch.equal(out[:, Hq + Hk:], qkv[:, Hq + Hk:])
+    # out-of-place into strided output views: bytes between rows stay as they were
+    src = gpu(workloads.random_rows(T, Hq, "bf16", 84))
+    canvas = torch.full((T, Hq + 64), 7.0, dtype=torch.bfloat16, device=DEV)
+    say("strided output view")
+    qk.forward(src, None, gpu(gq), None, out_q=canvas[:, 32:32 + Hq])
+    torch.cuda.synchronize()
+    c = canvas.cpu()
+    ref, _ = oracle.forward(src.cpu(), gq, 1e-6, 1)
+    assert_parity(c[:, 32:32 + Hq], ref, torch.bfloat16, "strided out")
+    assert (c[:, :32] == 7.0).all() and (c[:, 32 + Hq:] == 7.0).all()
+
+
+def test_special_rows():
+    """Zero rows give zeros; eps = 0 is allowed; a constant row gives
+    a / sqrt(a^2 + eps) * gamma; results are bit-reproducible."""
+    T, H = 8, 1024
+    x = workloads.random_rows(T, H, "f32", 91)
+    x[0] = 0.0
+    x[1] = 0.375
+    g = workloads.random_weights(H, "f32", 92)
+    for eps in (1e-6, 0.0):
+        say("special rows eps=%g" % eps)
+        xx = x.clone()
+        if eps == 0.0:
+            xx[0] = 1.0  # keep 0/0 out of it
+        y1, _ = run_forward(xx, None, g, None, eps, 1)
+        y2, _ = run_forward(xx, None, g, None, eps, 1)
+        assert torch.equal(y1, y2)
+        ref, _ = oracle.forward(xx, g, eps, 1)
+        assert_parity(y1, ref, torch.float32, "eps=%g" % eps)
+        if eps > 0:
+            assert (y1[0] == 0).all()
+
+
+def test_empty_and_single_tensor():
+    z = torch.empty((0, 4096), dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(4096, dtype=torch.bfloat16, device=DEV)
+    say("T=0")
+    yq, yk = qk.forward(z, z, g, g)
+    torch.cuda.synchronize()
+    assert yq.shape == (0, 4096)
