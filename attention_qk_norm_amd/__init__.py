@@ -40,7 +40,7 @@ class Rows(ctypes.Structure):
 class Options(ctypes.Structure):
     """qknorm_options: schedule overrides (0 = automatic)."""
     _fields_ = [("waves_per_row", ctypes.c_int), ("max_workgroups", ctypes.c_int),
-                ("nontemporal", ctypes.c_int)]
+                ("cached_rows", ctypes.c_int)]
 
 
 class QKNormError(RuntimeError):
@@ -99,9 +99,9 @@ def _check(status, where):
 class Context:
     """Owns a qknorm_ctx for one device (immutable, shareable by threads)."""
 
-    def __init__(self, device=0, waves_per_row=0, max_workgroups=0, nontemporal=0):
+    def __init__(self, device=0, waves_per_row=0, max_workgroups=0, cached_rows=0):
         self.device = int(device)
-        self.options = Options(int(waves_per_row), int(max_workgroups), int(nontemporal))
+        self.options = Options(int(waves_per_row), int(max_workgroups), int(cached_rows))
         h = ctypes.c_void_p()
         _check(lib().qknorm_create_ex(ctypes.byref(h), self.device, ctypes.byref(self.options)),
                "qknorm_create_ex")

@@ -163,8 +163,14 @@ struct SegIn {
   int K;
 };
 
-// Plans a launch of 1 or 2 segments. Returns QKNORM_OK or QKNORM_ERR_SHAPE.
-int plan_launch(const qknorm_ctx* ctx, const SegIn* in, int nseg, Plan* plans, int* nw) {
+// Plans a launch of 1 or 2 segments of T rows each. Returns QKNORM_OK or
+// QKNORM_ERR_SHAPE.
+//
+// The row width sets the smallest team that holds a row in registers. When
+// the launch has too few rows to give every SIMD of the chip a wavefront
+// (decode-sized batches), teams are widened, up to one workgroup per row, so
+// each row's loads are spread over more wavefronts and finish sooner.
+int plan_launch(const qknorm_ctx* ctx, const SegIn* in, int nseg, int64_t T, Plan* plans, int* nw) {
   const int fl = forced_log2(ctx);
   bool ok = true;
   bool wide = fl > 2;
@@ -176,10 +182,29 @@ int plan_launch(const qknorm_ctx* ctx, const SegIn* in, int nseg, Plan* plans, i
     ok = true;
     for (int i = 0; i < nseg && ok; ++i) ok = plan_segment(in[i].nvec, in[i].K, 4, kMaxSlots16, fl, &plans[i]);
     *nw = 16;
-  } else {
-    *nw = 4;
+    return ok ? QKNORM_OK : QKNORM_ERR_SHAPE;
   }
-  return ok ? QKNORM_OK : QKNORM_ERR_SHAPE;
+  *nw = 4;
+  if (!ok) return QKNORM_ERR_SHAPE;
+  if (fl < 0) {
+    const int64_t fill = int64_t{4} * ctx->num_cus;  // one wavefront per SIMD
+    for (;;) {
+      int64_t waves = 0;
+      for (int i = 0; i < nseg; ++i) waves += T << plans[i].wpr_log2;
+      if (waves >= fill) break;
+      bool widened = false;
+      for (int i = 0; i < nseg; ++i) {
+        const int wl = plans[i].wpr_log2 + 1;
+        if (wl > 2) continue;
+        plans[i].wpr_log2 = wl;
+        plans[i].slots = plans[i].masked ? plain_slots(in[i].nvec, wl)
+                                         : seg_slots(in[i].nvec / in[i].K, in[i].K, wl);
+        widened = true;
+      }
+      if (!widened) break;
+    }
+  }
+  return QKNORM_OK;
 }
 
 // Lay one segment's rows out over the team's lanes (see qknorm_launch.h).
@@ -219,15 +244,24 @@ void fill_layout(qkn::Seg* s, int wl, bool masked, int nw, int64_t nvec, int K, 
   }
 }
 
-int grid_for(const qknorm_ctx* ctx, int64_t total_wg) {
-  int64_t g = total_wg;
-  if (ctx->opt.max_workgroups > 0 && g > ctx->opt.max_workgroups) g = ctx->opt.max_workgroups;
-  return static_cast<int>(g);
-}
-
-int run(const qkn::Variant& v, const qkn::Args& a, int grid, void* stream) {
-  if (grid <= 0) return QKNORM_OK;
-  const hipError_t e = qkn::launch(v, a, grid, static_cast<hipStream_t>(stream));
+// Enqueue `nseg` segments: grid.x covers the larger segment (capped by the
+// persistent-grid option), grid.y selects the segment. A capped forward uses
+// the pipelined variant, whose workgroups prefetch their next rows.
+int run(const qknorm_ctx* ctx, qkn::Variant v, const qkn::Args& a, int nseg, void* stream) {
+  int64_t gx = 0;
+  for (int i = 0; i < nseg; ++i) gx = a.seg[i].nwg > gx ? a.seg[i].nwg : gx;
+  if (gx <= 0) return QKNORM_OK;
+  const int cap = ctx->opt.max_workgroups;
+  if (cap > 0 && gx > cap) {
+    gx = cap;
+    v.pipe = v.mode == qkn::MODE_FWD && v.nw == 4;
+  }
+  // a launch holds at most 2^32 - 1 work-items along x; the workgroups'
+  // grid-stride loop covers any rows beyond that
+  const int64_t hw_cap = int64_t{0xFFFFFFFF} / (int64_t{64} * v.nw);
+  if (gx > hw_cap) gx = hw_cap;
+  const hipError_t e = qkn::launch(v, a, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(nseg)),
+                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QKNORM_OK : QKNORM_ERR_DEVICE;
 }
 
@@ -265,7 +299,7 @@ int qknorm_create_ex(qknorm_ctx** ctx_out, int device, const qknorm_options* opt
     o = *opts;
     const int w = o.waves_per_row;
     if (!(w == 0 || w == 1 || w == 2 || w == 4 || w == 8 || w == 16) || o.max_workgroups < 0 ||
-        (o.nontemporal != 0 && o.nontemporal != 1))
+        (o.cached_rows != 0 && o.cached_rows != 1))
       return QKNORM_ERR_SHAPE;
   }
   int n = 0;
@@ -322,17 +356,15 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
   for (int i = 0; i < nseg; ++i) in[i] = SegIn{segs[i]->width / ve, num_slices};
   Plan plans[2];
   int nw = 4;
-  st = plan_launch(ctx, in, nseg, plans, &nw);
+  st = plan_launch(ctx, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) return st;
 
   bool masked = false;
   for (int i = 0; i < nseg; ++i) masked = masked || plans[i].masked;
   qkn::Args a{};
   a.T = T;
-  a.nseg = nseg;
   a.eps = eps;
   int slots = 0;
-  int64_t total = 0;
   for (int i = 0; i < nseg; ++i) {
     qkn::Seg& s = a.seg[i];
     s.x = segs[i]->x;
@@ -346,14 +378,11 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
     s.h = static_cast<float>(segs[i]->width);
     s.comb_k = 0;
     slots = s.nslot > slots ? s.nslot : slots;
-    total += s.nwg;
   }
-  if (total > kMaxRows) return QKNORM_ERR_SHAPE;
-  a.total_wg = static_cast<int32_t>(total);
   qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw), nw, masked,
-                 ctx->opt.nontemporal == 1 && !masked};
+                 ctx->opt.cached_rows == 0 || masked, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
-  return run(v, a, grid_for(ctx, total), stream);
+  return run(ctx, v, a, nseg, stream);
 }
 
 int qknorm_partial_stats(qknorm_ctx* ctx, int dtype, int64_t T, const void* x_slice, int64_t x_stride,
@@ -378,11 +407,10 @@ int qknorm_partial_stats(qknorm_ctx* ctx, int dtype, int64_t T, const void* x_sl
   const SegIn in{nvec, 1};
   Plan plan;
   int nw = 4;
-  st = plan_launch(ctx, &in, 1, &plan, &nw);
+  st = plan_launch(ctx, &in, 1, T, &plan, &nw);
   if (st != QKNORM_OK) return st;
   qkn::Args a{};
   a.T = T;
-  a.nseg = 1;
   a.eps = 0.0f;
   qkn::Seg& s = a.seg[0];
   s.x = x_slice;
@@ -390,10 +418,9 @@ int qknorm_partial_stats(qknorm_ctx* ctx, int dtype, int64_t T, const void* x_sl
   s.stats_out = out;
   fill_layout(&s, plan.wpr_log2, false, nw, nvec, 1, T);
   s.h = static_cast<float>(slice_width);
-  a.total_wg = s.nwg;
-  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(s.nslot, nw), nw, false, false};
+  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(s.nslot, nw), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
-  return run(v, a, grid_for(ctx, s.nwg), stream);
+  return run(ctx, v, a, 1, stream);
 }
 
 int qknorm_apply_stats(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* x_slice,
@@ -422,11 +449,10 @@ int qknorm_apply_stats(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows*
   const SegIn in{nvec, 1};
   Plan plan;
   int nw = 4;
-  st = plan_launch(ctx, &in, 1, &plan, &nw);
+  st = plan_launch(ctx, &in, 1, T, &plan, &nw);
   if (st != QKNORM_OK) return st;
   qkn::Args a{};
   a.T = T;
-  a.nseg = 1;
   a.eps = eps;
   qkn::Seg& s = a.seg[0];
   s.x = x_slice->x;
@@ -438,10 +464,9 @@ int qknorm_apply_stats(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows*
   fill_layout(&s, plan.wpr_log2, false, nw, nvec, 1, T);
   s.comb_k = num_slices;
   s.h = static_cast<float>(h_total);
-  a.total_wg = s.nwg;
-  qkn::Variant v{dtype, qkn::MODE_APPLY, qkn::compiled_vpl(s.nslot, nw), nw, false, false};
+  qkn::Variant v{dtype, qkn::MODE_APPLY, qkn::compiled_vpl(s.nslot, nw), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
-  return run(v, a, grid_for(ctx, s.nwg), stream);
+  return run(ctx, v, a, 1, stream);
 }
 
 }  // extern "C"

@@ -137,148 +137,285 @@ __device__ __forceinline__ int slice_of(int v, int sv, float inv_sv) {
   return q;
 }
 
+// Everything a wavefront reads from its segment's kernel arguments, copied
+// into scalar registers at kernel entry: the copy sits before any branch, so
+// the scalar loads issue together and retire in one round trip.
+struct Hot {
+  const void* x;
+  void* y;
+  const void* gamma;
+  const float* stats_in;
+  float* stats_out;
+  int64_t x_stride, y_stride, T;
+  int rows_per_wg, nwg, nslot, wpr_log2, lay_k, comb_k, slice_vec;
+  uint32_t row_bytes, flush_mask;
+  float inv_slice_vec, h, eps;
+
+  __device__ __forceinline__ Hot(const Args& a, const Seg& s)
+      : x(s.x), y(s.y), gamma(s.gamma), stats_in(s.stats_in), stats_out(s.stats_out),
+        x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
+        nslot(s.nslot), wpr_log2(s.wpr_log2),
+        lay_k(s.lay_k), comb_k(s.comb_k), slice_vec(s.slice_vec), row_bytes(s.row_bytes),
+        flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h), eps(a.eps) {}
+};
+
+// The segment's slot table, read at kernel entry with the other arguments.
+template <int VPL>
+struct Tables {
+  int lim[VPL];
+  int base[VPL];
+  __device__ __forceinline__ explicit Tables(const Seg& s) {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      lim[j] = s.slot_lim[j];
+      base[j] = s.slot_base[j];
+    }
+  }
+};
+
+// Where this lane's V slots sit in a row of one segment: fixed for the whole
+// launch, computed once per wavefront.
+template <int V>
+struct Layout {
+  int wpr_log2, wpr, team, tl;
+  uint32_t off[V];  // byte offset of each slot's vector; kOutside when empty
+  int base[V];      // vector index of each slot (masked layout)
+
+  template <int VPL>
+  __device__ __forceinline__ Layout(const Tables<VPL>& tb, int wl, int wave, int lane) {
+    static_assert(V <= VPL, "layout wider than its table");
+    wpr_log2 = wl;
+    wpr = 1 << wpr_log2;
+    team = wave >> wpr_log2;
+    tl = ((wave & (wpr - 1)) << 6) | lane;  // lane within the team
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      base[j] = tb.base[j];
+      const uint32_t o = static_cast<uint32_t>(tb.base[j] + tl) * 16u;
+      off[j] = tl < tb.lim[j] ? o : kOutside;
+    }
+  }
+};
+
+// Row `row` of the segment as a buffer resource; rows past T get an empty one.
+template <class E>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int64_t stride, int64_t row,
+                                                           bool live, uint32_t bytes) {
+  return rsrc(static_cast<const char*>(p) + row * stride * E::kBytes, live ? bytes : 0u);
+}
+
+template <class E, int VPL, bool NT>
+__device__ __forceinline__ void load_row(u32x4 (&d)[VPL], __amdgpu_buffer_rsrc_t r, const Layout<VPL>& L) {
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) d[j] = load16<NT>(r, L.off[j]);
+}
+
+// The row statistic S = sum over slices (ascending) of each slice's sum of
+// squares. Teams of several wavefronts add their partials through `part`
+// (one barrier); every lane of the team returns the same S.
+template <class E, int VPL, bool MASKED>
+__device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, const Layout<VPL>& L,
+                                          int wave, int lane, float* part) {
+  float S = 0.f;
+  if constexpr (!MASKED) {
+    // slots are grouped by slice; a set bit in flush_mask closes a slice
+    float p = 0.f;
+    int slice = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      p = E::sumsq(d[j], p);
+      if ((s.flush_mask >> j) & 1u) {
+        const float P = wave_sum(p);
+        p = 0.f;
+        if (L.wpr == 1)
+          S += P;
+        else if (lane == 0)
+          part[wave * kWave + slice] = P;
+        ++slice;
+      }
+    }
+  } else {
+    // plain strided slots; each vector's squares join the partial of the
+    // slice its index falls in
+    float q[VPL];
+    int sid[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      q[j] = E::sumsq(d[j], 0.f);
+      sid[j] = slice_of(L.base[j] + L.tl, s.slice_vec, s.inv_slice_vec);
+    }
+    for (int k = 0; k < s.lay_k; ++k) {
+      float p = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) p += (sid[j] == k) ? q[j] : 0.f;
+      const float P = wave_sum(p);
+      if (L.wpr == 1)
+        S += P;
+      else if (lane == 0)
+        part[wave * kWave + k] = P;
+    }
+  }
+  if (L.wpr > 1) {
+    __syncthreads();
+    const int w0 = L.team << L.wpr_log2;
+    for (int k = 0; k < s.lay_k; ++k) {
+      float P = 0.f;
+      for (int w = 0; w < L.wpr; ++w) P += part[(w0 + w) * kWave + k];
+      S += P;
+    }
+    __syncthreads();  // `part` is free again
+  }
+  return S;
+}
+
+template <class E, int VPL, bool NT>
+__device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const u32x4 (&g)[VPL], float S,
+                                            float h, float eps, __amdgpu_buffer_rsrc_t yr,
+                                            const Layout<VPL>& L) {
+  const float r = 1.0f / __builtin_sqrtf(S / h + eps);
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::scale(d[j], g[j], r));
+}
+
+// One row per team: load, statistic, scale, store.
 template <class E, int VPL, int MODE, bool MASKED, bool NT>
-__device__ __forceinline__ void row_pass(const Args& a, int si, int gl, int wave, int lane,
+__device__ __forceinline__ void row_pass(const Hot& s, const Layout<VPL>& L, int gi, int wave, int lane,
                                          float* part) {
-  const Seg& s = a.seg[si];
-  const int wpr_log2 = s.wpr_log2;
-  const int wpr = 1 << wpr_log2;
-  const int team = wave >> wpr_log2;
-  const int tl = ((wave & (wpr - 1)) << 6) | lane;  // lane within the team
-  const int64_t row = static_cast<int64_t>(gl) * s.rows_per_wg + team;
-  const bool live = row < a.T;
-  if (wpr == 1 && !live) return;  // no barrier to keep in step with
+  // rows past T read and write nothing (their buffer resources are empty);
+  // no branch here, so nothing delays the first loads
+  const int64_t row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
+  const bool live = row < s.T;
 
-  // byte offset of each slot's vector in the row; kOutside for empty slots
-  // (both table words are read unconditionally so the scalar loads batch up)
-  int lim[VPL], base[VPL];
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) {
-    lim[j] = s.slot_lim[j];
-    base[j] = s.slot_base[j];
-  }
-  uint32_t off[VPL];
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) {
-    const uint32_t o = static_cast<uint32_t>(base[j] + tl) * 16u;
-    off[j] = tl < lim[j] ? o : kOutside;
-  }
-
-  const uint32_t bytes = live ? s.row_bytes : 0u;
-  const auto xr = rsrc(static_cast<const char*>(s.x) + row * s.x_stride * E::kBytes, bytes);
-
-  // ---- 1. load the row, then its weights, into registers -------------------
   u32x4 d[VPL];
   u32x4 g[VPL];
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) d[j] = load16<NT>(xr, off[j]);
-  if constexpr (MODE != MODE_STATS) {
-    const auto gr = rsrc(s.gamma, bytes);
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) g[j] = load16<false>(gr, off[j]);
-  }
+  load_row<E, VPL, NT>(d, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
+  if constexpr (MODE != MODE_STATS) load_row<E, VPL, false>(g, rsrc(s.gamma, s.row_bytes), L);
 
-  // ---- 2./3. the row statistic ----------------------------------------------
   float S = 0.f;
   if constexpr (MODE == MODE_APPLY) {
     // lane k fetches partial k; then they are added in ascending k
     float pk = 0.f;
-    if (live && lane < s.comb_k) pk = s.stats_in[static_cast<int64_t>(lane) * a.T + row];
+    if (live && lane < s.comb_k) pk = s.stats_in[static_cast<int64_t>(lane) * s.T + row];
     for (int k = 0; k < s.comb_k; ++k) S += lane_value(pk, k);
   } else {
-    if constexpr (!MASKED) {
-      // slots are grouped by slice; a set bit in flush_mask closes a slice
-      float p = 0.f;
-      int slice = 0;
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        p = E::sumsq(d[j], p);
-        if ((s.flush_mask >> j) & 1u) {
-          const float P = wave_sum(p);
-          p = 0.f;
-          if (wpr == 1)
-            S += P;
-          else if (lane == 0)
-            part[wave * kWave + slice] = P;
-          ++slice;
-        }
-      }
-    } else {
-      // plain strided slots; each vector's squares join the partial of the
-      // slice its index falls in
-      float q[VPL];
-      int sid[VPL];
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        q[j] = E::sumsq(d[j], 0.f);
-        sid[j] = slice_of(base[j] + tl, s.slice_vec, s.inv_slice_vec);
-      }
-      for (int k = 0; k < s.lay_k; ++k) {
-        float p = 0.f;
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) p += (sid[j] == k) ? q[j] : 0.f;
-        const float P = wave_sum(p);
-        if (wpr == 1)
-          S += P;
-        else if (lane == 0)
-          part[wave * kWave + k] = P;
-      }
-    }
-    if (wpr > 1) {
-      __syncthreads();
-      const int w0 = team << wpr_log2;
-      for (int k = 0; k < s.lay_k; ++k) {
-        float P = 0.f;
-        for (int w = 0; w < wpr; ++w) P += part[(w0 + w) * kWave + k];
-        S += P;
-      }
-    }
+    S = row_stat<E, VPL, MASKED>(d, s, L, wave, lane, part);
   }
 
   if constexpr (MODE == MODE_STATS) {
-    if (live && tl == 0) s.stats_out[row] = S;
+    if (live && L.tl == 0) s.stats_out[row] = S;
   } else {
-    // ---- 4. scale and store ---------------------------------------------------
-    const float r = 1.0f / __builtin_sqrtf(S / s.h + a.eps);
-    const auto yr = rsrc(static_cast<char*>(s.y) + row * s.y_stride * E::kBytes, bytes);
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) store16<NT>(yr, off[j], E::scale(d[j], g[j], r));
+    scale_store<E, VPL, NT>(d, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
   }
-  if (wpr > 1) __syncthreads();  // the next row of this workgroup reuses `part`
 }
 
-template <class E, int VPL, int NW, int MODE, bool MASKED, bool NT>
+// Persistent workgroups: group gi, gi + G, gi + 2G, ... (G = gridDim.x). The
+// next group's rows are loaded before the current group is reduced and
+// stored, so reads of later rows overlap writes of earlier ones; gamma is
+// loaded once. Every wavefront of a workgroup runs the same number of
+// iterations (rows past T are empty), so barriers stay in step.
+template <class E, int VPL, bool MASKED, bool NT>
+__device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L,
+                                              int wave, int lane, float* part) {
+  const int G = gridDim.x;
+  int g0 = blockIdx.x;
+  if (g0 >= s.nwg) return;
+  u32x4 A[VPL], B[VPL], g[VPL];
+  int64_t ra = static_cast<int64_t>(g0) * s.rows_per_wg + L.team;
+  load_row<E, VPL, NT>(A, row_rsrc<E>(s.x, s.x_stride, ra, ra < s.T, s.row_bytes), L);
+  load_row<E, VPL, false>(g, rsrc(s.gamma, s.row_bytes), L);
+  for (;;) {
+    const int g1 = g0 + G;
+    const int64_t rb = static_cast<int64_t>(g1) * s.rows_per_wg + L.team;
+    load_row<E, VPL, NT>(B, row_rsrc<E>(s.x, s.x_stride, rb, g1 < s.nwg && rb < s.T, s.row_bytes), L);
+    float S = row_stat<E, VPL, MASKED>(A, s, L, wave, lane, part);
+    scale_store<E, VPL, NT>(A, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, ra, ra < s.T, s.row_bytes), L);
+    if (g1 >= s.nwg) break;
+    const int g2 = g1 + G;
+    ra = static_cast<int64_t>(g2) * s.rows_per_wg + L.team;
+    load_row<E, VPL, NT>(A, row_rsrc<E>(s.x, s.x_stride, ra, g2 < s.nwg && ra < s.T, s.row_bytes), L);
+    S = row_stat<E, VPL, MASKED>(B, s, L, wave, lane, part);
+    scale_store<E, VPL, NT>(B, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, rb, rb < s.T, s.row_bytes), L);
+    if (g2 >= s.nwg) break;
+    g0 = g2;
+  }
+}
+
+template <class E, int V, int VPL, int MODE, bool MASKED, bool NT, bool PIPE>
+__device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wave, int lane, float* part) {
+  const Layout<V> L(tb, s.wpr_log2, wave, lane);
+  if constexpr (PIPE) {
+    fwd_pipelined<E, V, MASKED, NT>(s, L, wave, lane, part);
+  } else {
+    // the first group needs no bounds check (a group past the end holds only
+    // empty rows), so its loads can follow the argument loads directly
+    int gi = blockIdx.x;
+    do {
+      row_pass<E, V, MODE, MASKED, NT>(s, L, gi, wave, lane, part);
+      gi += gridDim.x;
+    } while (gi < s.nwg);
+  }
+}
+
+// The variant is compiled for VPL slots, the widest segment of the launch;
+// a narrower segment (the key rows of a grouped-query layout) runs the body
+// for VPL/2, VPL/4, ... slots instead, chosen by one uniform branch, so it
+// issues no instructions for slots it does not have.
+template <class E, int V, int VPL, int MODE, bool MASKED, bool NT, bool PIPE>
+__device__ __forceinline__ void dispatch(const Hot& s, const Tables<VPL>& tb, int wave, int lane,
+                                         float* part) {
+  if constexpr (V > 1) {
+    if (s.nslot <= V / 2) {
+      dispatch<E, V / 2, VPL, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part);
+      return;
+    }
+  }
+  body<E, V, VPL, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part);
+}
+
+// blockIdx.y selects the segment (query rows, key rows), so everything a
+// wavefront needs from the kernel arguments is one round of scalar loads.
+template <class E, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE>
 __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   __shared__ float part[NW * kWave];  // per-wavefront slice partials (teams of > 1 wave)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-  const int nwg0 = a.seg[0].nwg;
-  for (int gi = blockIdx.x; gi < a.total_wg; gi += gridDim.x) {
-    const int si = gi >= nwg0 ? 1 : 0;
-    row_pass<E, VPL, MODE, MASKED, NT>(a, si, gi - si * nwg0, wave, lane, part);
-  }
+  const Seg& seg = a.seg[blockIdx.y];
+  const Hot s(a, seg);
+  const Tables<VPL> tb(seg);
+  dispatch<E, VPL, VPL, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part);
 }
 
 template <class E, int VPL, int NW>
-hipError_t launch_vpl(const Variant& v, const Args& a, int grid, hipStream_t st) {
-  const dim3 gd(grid), bd(NW * kWave);
+hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, hipStream_t st) {
+  const dim3 bd(NW * kWave);
   if (v.mode == MODE_FWD) {
+    if constexpr (NW == 4) {
+      if (v.pipe) {
+        if (v.masked)
+          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, true>), gd, bd, 0, st, a);
+        else if (v.nt)
+          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, true>), gd, bd, 0, st, a);
+        else
+          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false, true>), gd, bd, 0, st, a);
+        return hipGetLastError();
+      }
+    }
     if (v.masked)
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, false>), gd, bd, 0, st, a);
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, false>), gd, bd, 0, st, a);
     else if (v.nt)
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true>), gd, bd, 0, st, a);
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, false>), gd, bd, 0, st, a);
     else
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false>), gd, bd, 0, st, a);
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false, false>), gd, bd, 0, st, a);
   } else if (v.mode == MODE_STATS) {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, false, false>), gd, bd, 0, st, a);
+    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, false, true, false>), gd, bd, 0, st, a);
   } else {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_APPLY, false, false>), gd, bd, 0, st, a);
+    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_APPLY, false, true, false>), gd, bd, 0, st, a);
   }
   return hipGetLastError();
 }
 
 template <class E>
-hipError_t launch_dtype(const Variant& v, const Args& a, int grid, hipStream_t st) {
+hipError_t launch_dtype(const Variant& v, const Args& a, dim3 grid, hipStream_t st) {
   if (v.nw == 4) {
     switch (v.vpl) {
       case 1: return launch_vpl<E, 1, 4>(v, a, grid, st);
@@ -319,7 +456,7 @@ int compiled_vpl(int slots, int nw) {
   return 0;
 }
 
-hipError_t launch(const Variant& v, const Args& a, int grid, hipStream_t stream) {
+hipError_t launch(const Variant& v, const Args& a, dim3 grid, hipStream_t stream) {
   if (v.dtype == QKNORM_F32) return launch_dtype<F32>(v, a, grid, stream);
   if (v.dtype == QKNORM_BF16) return launch_dtype<BF16>(v, a, grid, stream);
   return hipErrorInvalidValue;

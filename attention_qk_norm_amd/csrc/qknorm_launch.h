@@ -56,10 +56,8 @@ struct Seg {
 };
 
 struct Args {
-  Seg seg[2];
-  int64_t T;         // rows per segment
-  int32_t nseg;      // 1 or 2
-  int32_t total_wg;  // seg[0].nwg + seg[1].nwg (when nseg == 2)
+  Seg seg[2];  // blockIdx.y selects one
+  int64_t T;   // rows per segment
   float eps;
 };
 
@@ -71,13 +69,15 @@ struct Variant {
   int nw;        // wavefronts per workgroup: 4 or 16
   bool masked;   // FWD only: masked layout
   bool nt;       // FWD only: non-temporal row loads and stores
+  bool pipe;     // FWD only: persistent workgroups with the next rows prefetched
 };
 
 // Smallest compiled slot count >= `slots` for `nw` wavefronts per workgroup,
 // or 0 when none is large enough.
 int compiled_vpl(int slots, int nw);
 
-// Enqueue one launch of `grid` workgroups. Returns hipSuccess or the launch error.
-hipError_t launch(const Variant& v, const Args& a, int grid, hipStream_t stream);
+// Enqueue one launch: grid.x workgroups per segment, grid.y segments.
+// Returns hipSuccess or the launch error.
+hipError_t launch(const Variant& v, const Args& a, dim3 grid, hipStream_t stream);
 
 }  // namespace qkn

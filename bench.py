@@ -8,8 +8,11 @@ key rows of 4096 bf16, Laplace(0, 1) values, 8 column slices, in-place
 output), the one measured against the HBM roofline. Buffer sets are rotated
 so that no launch finds its data in the 256 MB Infinity Cache.
 
-Prints one JSON line. Kernel time comes from HIP events recorded around
-every launch on the stream the kernel runs on (torch's current stream).
+Prints one JSON line. The timed region is K launches back to back on the
+stream the kernel runs on (torch's current stream), bracketed by HIP events;
+a spin kernel queued ahead of it keeps the host's launch rate out of the
+measurement. The per-launch average of that region is the kernel time used
+for the roofline.
 """
 import argparse
 import hashlib
@@ -39,6 +42,17 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
+def calibrate_sleep(torch, stream):
+    """Spin-kernel cycles per microsecond on this device."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    e0.record(stream)
+    torch.cuda._sleep(2_000_000)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 2_000_000 / max(e0.elapsed_time(e1) * 1e3, 1.0)
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -54,7 +68,7 @@ def parse():
                    help="approximate CPU time spent timing the oracle")
     p.add_argument("--waves-per-row", type=int, default=0)
     p.add_argument("--max-workgroups", type=int, default=0)
-    p.add_argument("--nontemporal", type=int, default=0)
+    p.add_argument("--cached-rows", type=int, default=0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also launch a plain elementwise copy of known size (counter calibration)")
     p.add_argument("--quiet", action="store_true")
@@ -141,7 +155,7 @@ def main():
     log(args, "%d buffer sets, %.0f MiB" % (nsets, nsets * set_bytes / 2**20))
 
     ctx = qk.Context(0, waves_per_row=args.waves_per_row, max_workgroups=args.max_workgroups,
-                     nontemporal=args.nontemporal)
+                     cached_rows=args.cached_rows)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, num_slices=K):
@@ -163,64 +177,58 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K launches, an event pair around each
+    # The GPU first runs a spin kernel long enough for the host to enqueue all
+    # timed launches behind it, so the timed region measures back-to-back
+    # kernels, not the host's launch rate.
+    cyc_per_us = calibrate_sleep(torch, stream)
+
+    def timed(n, fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(cyc_per_us * (200.0 + 40.0 * n)))
+        e0.record(stream)
+        h0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        host_us = (time.perf_counter() - h0) * 1e6
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, host_us
+
+    # timed region: K launches back to back, bracketed by events
+    ms_per_step, host_us = timed(args.steps, step)
+    kern_ms = ms_per_step
+
+    # per-launch event pairs (they add a little time of their own): spread only
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    region0, region1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    region0.record(stream)
     for i in range(args.steps):
         starts[i].record(stream)
         step(i)
         ends[i].record(stream)
-    region1.record(stream)
     torch.cuda.synchronize()
-    region_ms = region0.elapsed_time(region1)
-    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    kern_ms_mean = sum(per) / len(per)
-    kern_ms_p50 = per[len(per) // 2]
-    ms_per_step = region_ms / args.steps
-
-    # back-to-back launches without per-launch events (throughput as a caller sees it)
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    b0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    b2b_ms = b0.elapsed_time(b1) / args.steps
+    per = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
+    ev_p10, ev_p50, ev_p90 = per[len(per) // 10], per[len(per) // 2], per[(9 * len(per)) // 10]
 
     # the other slicing of the same workload, and a same-bytes device copy
     extra = {}
     for k_alt in w.slices:
         if k_alt == K:
             continue
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for i in range(args.warmup):
             step(i, k_alt)
-        e0.record(stream)
-        for i in range(args.steps):
-            step(i, k_alt)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        extra["ms_per_step_K%d" % k_alt] = e0.elapsed_time(e1) / args.steps
+        extra["kernel_us_K%d" % k_alt] = timed(args.steps, lambda i: step(i, k_alt))[0] * 1e3
     nb = w.T * (w.hq + w.hk) * eb
     csets = max(2, math.ceil(args.rotate_mib * 2**20 / (2 * nb)))
     cbufs = [(torch.empty(nb, dtype=torch.uint8, device=dev), torch.empty(nb, dtype=torch.uint8, device=dev))
              for _ in range(csets)]
-    for s, t in cbufs:
-        t.copy_(s)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for i in range(args.steps):
-        s, t = cbufs[i % csets]
-        t.copy_(s)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = c0.elapsed_time(c1) / args.steps
+    for s_, t_ in cbufs:
+        t_.copy_(s_)
+    copy_ms = timed(args.steps, lambda i: cbufs[i % csets][1].copy_(cbufs[i % csets][0]))[0]
     del cbufs
 
-    achieved_gbs = algo_bytes / (kern_ms_mean * 1e-3) / 1e9
+    achieved_gbs = algo_bytes / (kern_ms * 1e-3) / 1e9
     traffic = None
     tf = os.path.join(ROOT, TRAFFIC_FILE.format(workload=args.workload))
     if os.path.exists(tf):
@@ -250,9 +258,9 @@ def main():
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic},
         "hbm_gbs": achieved_gbs,
         "algorithmic_bytes_per_launch": algo_bytes,
-        "kernel_us_mean": kern_ms_mean * 1e3,
-        "kernel_us_p50": kern_ms_p50 * 1e3,
-        "back_to_back_us": b2b_ms * 1e3,
+        "kernel_us": kern_ms * 1e3,
+        "host_enqueue_us_per_launch": host_us / args.steps,
+        "event_pair_us_p10_p50_p90": [ev_p10 * 1e3, ev_p50 * 1e3, ev_p90 * 1e3],
         "copy_same_bytes_us": copy_ms * 1e3,
         "copy_same_bytes_gbs": 2 * nb / (copy_ms * 1e-3) / 1e9,
         "kernel_source_sha": kernel_source_sha(),

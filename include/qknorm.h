@@ -96,8 +96,9 @@ typedef struct qknorm_options {
                             share one row (1 = several rows per workgroup)      */
     int max_workgroups;  /* 0 = one workgroup per group of rows; > 0 caps the grid
                             and workgroups loop over rows (persistent grid)     */
-    int nontemporal;     /* 0 = default, 1 = streaming (non-temporal) loads and
-                            stores for the row data                             */
+    int cached_rows;     /* 0 = stream the row data (non-temporal loads and
+                            stores, the default); 1 = ordinary cached accesses
+                            (rows cut into many narrow slices always stream)   */
 } qknorm_options;
 
 /* Create a context for `device` (a HIP device ordinal) with default options.

@@ -221,13 +221,17 @@ def test_ragged_shapes(dtype, T, Hq, Hk, K):
 @pytest.mark.parametrize("opts", [dict(waves_per_row=1), dict(waves_per_row=2), dict(waves_per_row=4),
                                   dict(waves_per_row=8), dict(waves_per_row=16),
                                   dict(max_workgroups=7), dict(max_workgroups=300, waves_per_row=2),
-                                  dict(nontemporal=1)],
+                                  dict(max_workgroups=1), dict(max_workgroups=33, cached_rows=1),
+                                  dict(max_workgroups=5, waves_per_row=4),
+                                  dict(max_workgroups=3, waves_per_row=16),
+                                  dict(cached_rows=1)],
                          ids=lambda o: ",".join("%s=%s" % kv for kv in o.items()))
 def test_schedules_agree(opts):
     """Every schedule (team size, persistent grid, streaming stores) computes
     the same rows."""
     ctx = qk.Context(0, **opts)
-    for dtype, T, Hq, Hk, K in (("bf16", 131, 5120, 1024, 4), ("f32", 45, 2048, 512, 2)):
+    for dtype, T, Hq, Hk, K in (("bf16", 131, 5120, 1024, 4), ("f32", 45, 2048, 512, 2),
+                                ("bf16", 70, 4096, 4096, 64), ("bf16", 19, 1000, 8, 1)):
         q = workloads.random_rows(T, Hq, dtype, [7, T])
         k = workloads.random_rows(T, Hk, dtype, [8, T])
         gq = workloads.random_weights(Hq, dtype, 9)
