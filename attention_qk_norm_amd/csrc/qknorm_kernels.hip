@@ -147,14 +147,14 @@ struct Hot {
   const float* stats_in;
   float* stats_out;
   int64_t x_stride, y_stride, T;
-  int rows_per_wg, nwg, nslot, wpr_log2, lay_k, comb_k, slice_vec;
+  int rows_per_wg, nwg, nslot, wpr_log2, sub_log2, lds_gamma, lay_k, comb_k, slice_vec;
   uint32_t row_bytes, flush_mask;
   float inv_slice_vec, h, eps;
 
   __device__ __forceinline__ Hot(const Args& a, const Seg& s)
       : x(s.x), y(s.y), gamma(s.gamma), stats_in(s.stats_in), stats_out(s.stats_out),
         x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
-        nslot(s.nslot), wpr_log2(s.wpr_log2),
+        nslot(s.nslot), wpr_log2(s.wpr_log2), sub_log2(s.sub_log2), lds_gamma(s.lds_gamma),
         lay_k(s.lay_k), comb_k(s.comb_k), slice_vec(s.slice_vec), row_bytes(s.row_bytes),
         flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h), eps(a.eps) {}
 };
@@ -174,25 +174,29 @@ struct Tables {
 };
 
 // Where this lane's V slots sit in a row of one segment: fixed for the whole
-// launch, computed once per wavefront.
+// launch, computed once per wavefront. A team of 2^wpr_log2 wavefronts owns
+// a row; it is split into sub-teams of 2^sub_log2 wavefronts, and the row's
+// slices are dealt to the sub-teams round-robin, so slices narrower than the
+// team still keep every lane busy.
 template <int V>
 struct Layout {
   int wpr_log2, wpr, team, tl;
   uint32_t off[V];  // byte offset of each slot's vector; kOutside when empty
-  int base[V];      // vector index of each slot (masked layout)
+  int base[V];      // vector index of each slot, also when empty (masked layout)
 
   template <int VPL>
-  __device__ __forceinline__ Layout(const Tables<VPL>& tb, int wl, int wave, int lane) {
+  __device__ __forceinline__ Layout(const Tables<VPL>& tb, const Hot& s, int wave, int lane) {
     static_assert(V <= VPL, "layout wider than its table");
-    wpr_log2 = wl;
+    wpr_log2 = s.wpr_log2;
     wpr = 1 << wpr_log2;
     team = wave >> wpr_log2;
     tl = ((wave & (wpr - 1)) << 6) | lane;  // lane within the team
+    const int sub = (tl >> 6) >> s.sub_log2;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      base[j] = tb.base[j];
-      const uint32_t o = static_cast<uint32_t>(tb.base[j] + tl) * 16u;
-      off[j] = tl < tb.lim[j] ? o : kOutside;
+      base[j] = tb.base[j] + sub * s.slice_vec + (tl & ((64 << s.sub_log2) - 1));
+      const int v = slot_vector(tb.lim[j], tb.base[j], tl, wpr_log2, s.sub_log2, s.slice_vec, s.lay_k);
+      off[j] = v >= 0 ? static_cast<uint32_t>(v) * 16u : kOutside;
     }
   }
 };
@@ -242,7 +246,7 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       q[j] = E::sumsq(d[j], 0.f);
-      sid[j] = slice_of(L.base[j] + L.tl, s.slice_vec, s.inv_slice_vec);
+      sid[j] = slice_of(L.base[j], s.slice_vec, s.inv_slice_vec);
     }
     for (int k = 0; k < s.lay_k; ++k) {
       float p = 0.f;
@@ -256,13 +260,21 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
     }
   }
   if (L.wpr > 1) {
+    // slice k's partial comes from the wavefronts of sub-team k % nsub, at
+    // index k / nsub of their partial lists; slices are added in ascending k
+    // lane k gathers slice k's partials (one LDS round trip for all lanes),
+    // then the slices are added in ascending k
     __syncthreads();
     const int w0 = L.team << L.wpr_log2;
-    for (int k = 0; k < s.lay_k; ++k) {
-      float P = 0.f;
-      for (int w = 0; w < L.wpr; ++w) P += part[(w0 + w) * kWave + k];
-      S += P;
+    const int sub_log2 = MASKED ? L.wpr_log2 : s.sub_log2;
+    const int nsub_log2 = L.wpr_log2 - sub_log2;
+    float Pk = 0.f;
+    if (lane < s.lay_k) {
+      const int w1 = w0 + ((lane & ((1 << nsub_log2) - 1)) << sub_log2);
+      const int i = lane >> nsub_log2;
+      for (int w = 0; w < (1 << sub_log2); ++w) Pk += part[(w1 + w) * kWave + i];
     }
+    for (int k = 0; k < s.lay_k; ++k) S += lane_value(Pk, k);
     __syncthreads();  // `part` is free again
   }
   return S;
@@ -277,20 +289,12 @@ __device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const u32x4 (
   for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::scale(d[j], g[j], r));
 }
 
-// One row per team: load, statistic, scale, store.
+// Finish one row whose data (and weights) are in registers: statistic (or
+// the precomputed partials), then scale and store, or publish the statistic.
 template <class E, int VPL, int MODE, bool MASKED, bool NT>
-__device__ __forceinline__ void row_pass(const Hot& s, const Layout<VPL>& L, int gi, int wave, int lane,
-                                         float* part) {
-  // rows past T read and write nothing (their buffer resources are empty);
-  // no branch here, so nothing delays the first loads
-  const int64_t row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
-  const bool live = row < s.T;
-
-  u32x4 d[VPL];
-  u32x4 g[VPL];
-  load_row<E, VPL, NT>(d, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
-  if constexpr (MODE != MODE_STATS) load_row<E, VPL, false>(g, rsrc(s.gamma, s.row_bytes), L);
-
+__device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const u32x4 (&g)[VPL], const Hot& s,
+                                           const Layout<VPL>& L, int64_t row, bool live, int wave,
+                                           int lane, float* part) {
   float S = 0.f;
   if constexpr (MODE == MODE_APPLY) {
     // lane k fetches partial k; then they are added in ascending k
@@ -300,12 +304,45 @@ __device__ __forceinline__ void row_pass(const Hot& s, const Layout<VPL>& L, int
   } else {
     S = row_stat<E, VPL, MASKED>(d, s, L, wave, lane, part);
   }
-
   if constexpr (MODE == MODE_STATS) {
     if (live && L.tl == 0) s.stats_out[row] = S;
   } else {
     scale_store<E, VPL, NT>(d, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
   }
+}
+
+// Weights for the team's slots when several rows share a workgroup: the
+// workgroup copies gamma into LDS once, by direct buffer-to-LDS loads (no
+// VGPRs involved), and every wavefront reads its slots from there. That is
+// one global read of gamma per workgroup instead of one per row. The copy is
+// issued before the row loads (gamma_to_lds), and waited for after them
+// (gamma_from_lds), so it overlaps the row transfer. The LDS block is
+// rounded up to whole NW * 64 * 16-byte chunks, so lanes past the end of
+// gamma (which read zeros) still write inside it.
+template <int VPL, int NW>
+__device__ __forceinline__ void gamma_to_lds(const Hot& s, int wave, int lane, u32x4* lds_g) {
+  // rows_per_wg > 1 here, so a row has at most VPL * NW * 64 / 2 vectors
+  constexpr int kChunks = (VPL + 1) / 2;
+  const auto gr = rsrc(s.gamma, s.row_bytes);
+  const uint32_t nvec = s.row_bytes >> 4;
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    const uint32_t v0 = static_cast<uint32_t>(wave * kWave + k * NW * kWave);
+    if (v0 < nvec)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (__attribute__((address_space(3))) void*)(lds_g + v0), 16,
+                                               (v0 + static_cast<uint32_t>(lane)) * 16u, 0, 0, 0);
+  }
+}
+
+// Wait for this wavefront's copies (issued before its VPL row loads, so at
+// most VPL loads may stay in flight), then for the whole workgroup's.
+template <int VPL>
+__device__ __forceinline__ void gamma_from_lds(u32x4 (&g)[VPL], const Layout<VPL>& L, const u32x4* lds_g) {
+  // s_waitcnt with vmcnt = VPL and the lgkm / exp counters left alone
+  __builtin_amdgcn_s_waitcnt((VPL & 0xF) | ((VPL >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) g[j] = lds_g[L.off[j] == kOutside ? 0u : (L.off[j] >> 4)];
 }
 
 // Persistent workgroups: group gi, gi + G, gi + 2G, ... (G = gridDim.x). The
@@ -340,19 +377,40 @@ __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L
   }
 }
 
-template <class E, int V, int VPL, int MODE, bool MASKED, bool NT, bool PIPE>
-__device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wave, int lane, float* part) {
-  const Layout<V> L(tb, s.wpr_log2, wave, lane);
+template <class E, int V, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE>
+__device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wave, int lane, float* part,
+                                     u32x4* lds_g) {
+  const Layout<V> L(tb, s, wave, lane);
   if constexpr (PIPE) {
     fwd_pipelined<E, V, MASKED, NT>(s, L, wave, lane, part);
   } else {
-    // the first group needs no bounds check (a group past the end holds only
-    // empty rows), so its loads can follow the argument loads directly
+    // The first group needs no bounds check (a group past the end holds only
+    // empty rows), so its loads follow the argument loads directly.
     int gi = blockIdx.x;
-    do {
-      row_pass<E, V, MODE, MASKED, NT>(s, L, gi, wave, lane, part);
-      gi += gridDim.x;
-    } while (gi < s.nwg);
+    int64_t row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
+    bool live = row < s.T;
+    u32x4 d[V], g[V];
+    const bool staged = MODE != MODE_STATS && s.lds_gamma;
+    if (staged) gamma_to_lds<V, NW>(s, wave, lane, lds_g);
+    load_row<E, V, NT>(d, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
+    if constexpr (MODE != MODE_STATS) {
+      if (staged)
+        gamma_from_lds<V>(g, L, lds_g);
+      else
+        load_row<E, V, false>(g, rsrc(s.gamma, s.row_bytes), L);
+    }
+    row_finish<E, V, MODE, MASKED, NT>(d, g, s, L, row, live, wave, lane, part);
+    // Only grids capped at the hardware limit get here. Reloading gamma each
+    // time keeps the first row's registers free of this loop (holding them
+    // across it costs about 40 VGPRs).
+    for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
+      row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
+      live = row < s.T;
+      u32x4 d2[V], g2[V];
+      load_row<E, V, NT>(d2, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
+      if constexpr (MODE != MODE_STATS) load_row<E, V, false>(g2, rsrc(s.gamma, s.row_bytes), L);
+      row_finish<E, V, MODE, MASKED, NT>(d2, g2, s, L, row, live, wave, lane, part);
+    }
   }
 }
 
@@ -360,16 +418,16 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
 // a narrower segment (the key rows of a grouped-query layout) runs the body
 // for VPL/2, VPL/4, ... slots instead, chosen by one uniform branch, so it
 // issues no instructions for slots it does not have.
-template <class E, int V, int VPL, int MODE, bool MASKED, bool NT, bool PIPE>
+template <class E, int V, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE>
 __device__ __forceinline__ void dispatch(const Hot& s, const Tables<VPL>& tb, int wave, int lane,
-                                         float* part) {
+                                         float* part, u32x4* lds_g) {
   if constexpr (V > 1) {
     if (s.nslot <= V / 2) {
-      dispatch<E, V / 2, VPL, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part);
+      dispatch<E, V / 2, VPL, NW, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part, lds_g);
       return;
     }
   }
-  body<E, V, VPL, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part);
+  body<E, V, VPL, NW, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part, lds_g);
 }
 
 // blockIdx.y selects the segment (query rows, key rows), so everything a
@@ -377,64 +435,65 @@ __device__ __forceinline__ void dispatch(const Hot& s, const Tables<VPL>& tb, in
 template <class E, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE>
 __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   __shared__ float part[NW * kWave];  // per-wavefront slice partials (teams of > 1 wave)
+  extern __shared__ u32x4 lds_g[];    // staged gamma (dynamic size: the launch's widest row)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   const Seg& seg = a.seg[blockIdx.y];
   const Hot s(a, seg);
   const Tables<VPL> tb(seg);
-  dispatch<E, VPL, VPL, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part);
+  dispatch<E, VPL, VPL, NW, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part, lds_g);
 }
 
 template <class E, int VPL, int NW>
-hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, hipStream_t st) {
+hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
   const dim3 bd(NW * kWave);
   if (v.mode == MODE_FWD) {
     if constexpr (NW == 4) {
       if (v.pipe) {
         if (v.masked)
-          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, true>), gd, bd, 0, st, a);
+          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, true>), gd, bd, lds, st, a);
         else if (v.nt)
-          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, true>), gd, bd, 0, st, a);
+          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, true>), gd, bd, lds, st, a);
         else
-          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false, true>), gd, bd, 0, st, a);
+          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false, true>), gd, bd, lds, st, a);
         return hipGetLastError();
       }
     }
     if (v.masked)
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, false>), gd, bd, 0, st, a);
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, false>), gd, bd, lds, st, a);
     else if (v.nt)
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, false>), gd, bd, 0, st, a);
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, false>), gd, bd, lds, st, a);
     else
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false, false>), gd, bd, 0, st, a);
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false, false>), gd, bd, lds, st, a);
   } else if (v.mode == MODE_STATS) {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, false, true, false>), gd, bd, 0, st, a);
+    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, false, true, false>), gd, bd, lds, st, a);
   } else {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_APPLY, false, true, false>), gd, bd, 0, st, a);
+    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_APPLY, false, true, false>), gd, bd, lds, st, a);
   }
   return hipGetLastError();
 }
 
 template <class E>
-hipError_t launch_dtype(const Variant& v, const Args& a, dim3 grid, hipStream_t st) {
+hipError_t launch_dtype(const Variant& v, const Args& a, dim3 grid, unsigned lds, hipStream_t st) {
   if (v.nw == 4) {
     switch (v.vpl) {
-      case 1: return launch_vpl<E, 1, 4>(v, a, grid, st);
-      case 2: return launch_vpl<E, 2, 4>(v, a, grid, st);
-      case 4: return launch_vpl<E, 4, 4>(v, a, grid, st);
-      case 6: return launch_vpl<E, 6, 4>(v, a, grid, st);
-      case 8: return launch_vpl<E, 8, 4>(v, a, grid, st);
-      case 10: return launch_vpl<E, 10, 4>(v, a, grid, st);
-      case 12: return launch_vpl<E, 12, 4>(v, a, grid, st);
-      case 16: return launch_vpl<E, 16, 4>(v, a, grid, st);
+      case 1: return launch_vpl<E, 1, 4>(v, a, grid, lds, st);
+      case 2: return launch_vpl<E, 2, 4>(v, a, grid, lds, st);
+      case 4: return launch_vpl<E, 4, 4>(v, a, grid, lds, st);
+      case 6: return launch_vpl<E, 6, 4>(v, a, grid, lds, st);
+      case 8: return launch_vpl<E, 8, 4>(v, a, grid, lds, st);
+      case 10: return launch_vpl<E, 10, 4>(v, a, grid, lds, st);
+      case 12: return launch_vpl<E, 12, 4>(v, a, grid, lds, st);
+      case 16: return launch_vpl<E, 16, 4>(v, a, grid, lds, st);
       default: return hipErrorInvalidValue;
     }
   }
   if (v.nw == 16) {
     switch (v.vpl) {
-      case 1: return launch_vpl<E, 1, 16>(v, a, grid, st);
-      case 2: return launch_vpl<E, 2, 16>(v, a, grid, st);
-      case 4: return launch_vpl<E, 4, 16>(v, a, grid, st);
-      case 8: return launch_vpl<E, 8, 16>(v, a, grid, st);
+      case 1: return launch_vpl<E, 1, 16>(v, a, grid, lds, st);
+      case 2: return launch_vpl<E, 2, 16>(v, a, grid, lds, st);
+      case 4: return launch_vpl<E, 4, 16>(v, a, grid, lds, st);
+      case 8: return launch_vpl<E, 8, 16>(v, a, grid, lds, st);
       default: return hipErrorInvalidValue;
     }
   }
@@ -443,22 +502,9 @@ hipError_t launch_dtype(const Variant& v, const Args& a, dim3 grid, hipStream_t 
 
 }  // namespace
 
-int compiled_vpl(int slots, int nw) {
-  static const int k4[] = {1, 2, 4, 6, 8, 10, 12, 16};
-  static const int k16[] = {1, 2, 4, 8};
-  if (nw == 4) {
-    for (int c : k4)
-      if (c >= slots) return c;
-  } else if (nw == 16) {
-    for (int c : k16)
-      if (c >= slots) return c;
-  }
-  return 0;
-}
-
-hipError_t launch(const Variant& v, const Args& a, dim3 grid, hipStream_t stream) {
-  if (v.dtype == QKNORM_F32) return launch_dtype<F32>(v, a, grid, stream);
-  if (v.dtype == QKNORM_BF16) return launch_dtype<BF16>(v, a, grid, stream);
+hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t stream) {
+  if (v.dtype == QKNORM_F32) return launch_dtype<F32>(v, a, grid, lds_bytes, stream);
+  if (v.dtype == QKNORM_BF16) return launch_dtype<BF16>(v, a, grid, lds_bytes, stream);
   return hipErrorInvalidValue;
 }
 

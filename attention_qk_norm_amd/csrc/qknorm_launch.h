@@ -30,6 +30,10 @@ enum Mode : int {
 
 constexpr int kMaxSlots = 16;  // slots per lane of the widest compiled variant
 
+// Slot tables: slot j of sub-team 0 starts at vector slot_base[j] of the
+// row; slot_lim[j] packs the lanes it covers (low 16 bits) and which of the
+// sub-team's slices it belongs to (high 16 bits). Sub-team u adds
+// u * slice_vec to the base and owns slices u, u + nsub, u + 2 nsub, ...
 struct Seg {
   const void* x;          // row 0 of the input
   void* y;                // row 0 of the output (FWD, APPLY)
@@ -39,6 +43,8 @@ struct Seg {
   int64_t x_stride;       // elements between input rows
   int64_t y_stride;       // elements between output rows
   int32_t wpr_log2;       // log2 of the wavefronts per team
+  int32_t sub_log2;       // log2 of the wavefronts per sub-team (deals one slice)
+  int32_t lds_gamma;      // 1: the workgroup stages gamma in LDS and its rows share it
   int32_t rows_per_wg;    // teams per workgroup
   int32_t nwg;            // workgroups covering all T rows
   int32_t nslot;          // slots per lane in use
@@ -49,10 +55,8 @@ struct Seg {
   float inv_slice_vec;    // masked layout: 1.0f / slice_vec
   float h;                // the mean of squares divides by this width
   uint32_t flush_mask;    // segmented layout: bit j set when slot j ends a slice
-  // Slot j of team lane `tl` holds vector slot_base[j] + tl of the row when
-  // tl < slot_lim[j], and nothing otherwise (slot_lim[j] = 0 for j >= nslot).
   int32_t slot_base[kMaxSlots];
-  int32_t slot_lim[kMaxSlots];
+  int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
 };
 
 struct Args {
@@ -60,6 +64,17 @@ struct Args {
   int64_t T;   // rows per segment
   float eps;
 };
+
+// The row vector that slot j of team lane `tl` holds, or -1 when the slot is
+// empty there. `lim_word` and `base` are the slot's table entries. Used by
+// the kernels and by the host-side layout checks.
+__host__ __device__ inline int slot_vector(int lim_word, int base, int tl, int wpr_log2, int sub_log2,
+                                           int slice_vec, int K) {
+  const int sub = (tl >> 6) >> sub_log2;         // sub-team within the team
+  const int stl = tl & ((64 << sub_log2) - 1);  // lane within the sub-team
+  const int slice = sub + ((lim_word >> 16) << (wpr_log2 - sub_log2));
+  return (stl < (lim_word & 0xffff) && slice < K) ? base + sub * slice_vec + stl : -1;
+}
 
 // Compile-time variants a launch picks from.
 struct Variant {
@@ -72,12 +87,26 @@ struct Variant {
   bool pipe;     // FWD only: persistent workgroups with the next rows prefetched
 };
 
+// Slot counts the kernels are compiled for, per workgroup size.
+constexpr int kVpl4[] = {1, 2, 4, 6, 8, 10, 12, 16};
+constexpr int kVpl16[] = {1, 2, 4, 8};
+
 // Smallest compiled slot count >= `slots` for `nw` wavefronts per workgroup,
 // or 0 when none is large enough.
-int compiled_vpl(int slots, int nw);
+inline int compiled_vpl(int slots, int nw) {
+  if (nw == 4) {
+    for (int c : kVpl4)
+      if (c >= slots) return c;
+  } else if (nw == 16) {
+    for (int c : kVpl16)
+      if (c >= slots) return c;
+  }
+  return 0;
+}
 
-// Enqueue one launch: grid.x workgroups per segment, grid.y segments.
-// Returns hipSuccess or the launch error.
-hipError_t launch(const Variant& v, const Args& a, dim3 grid, hipStream_t stream);
+// Enqueue one launch: grid.x workgroups per segment, grid.y segments, with
+// `lds_bytes` of dynamic LDS for staged gamma. Returns hipSuccess or the
+// launch error.
+hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t stream);
 
 }  // namespace qkn

@@ -1,0 +1,165 @@
+// Host-side check of the launch planner and the slot tables (no GPU).
+//
+// Includes the library's host source, replaces the device launch with a
+// recorder, and for a grid of row widths, slice counts, row counts and team
+// sizes verifies, through the same slot_vector() the kernels use, that:
+//  - every vector of a row is held by exactly one (lane, slot) of its team;
+//  - each slot of a sub-team lies inside one slice;
+//  - a sub-team's slots of one slice are consecutive and the last one has
+//    its flush bit set, and the i-th flush is slice sub + i * nsub, which is
+//    where the LDS combine looks for it;
+//  - the slot count fits a compiled variant, and staged gamma fits the
+//    copy loop's bound.
+#include "qknorm_api.cpp"
+
+#include <cstdio>
+#include <vector>
+
+namespace qkn {
+static Variant g_v;
+static Args g_a;
+static dim3 g_grid;
+static unsigned g_lds;
+hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t) {
+  g_v = v;
+  g_a = a;
+  g_grid = grid;
+  g_lds = lds_bytes;
+  return hipSuccess;
+}
+}  // namespace qkn
+
+static int failures = 0;
+#define CHECK(c, ...)                          \
+  do {                                         \
+    if (!(c)) {                                \
+      if (failures < 20) {                     \
+        std::printf("FAIL %s: ", #c);          \
+        std::printf(__VA_ARGS__);              \
+        std::printf("\n");                    \
+      }                                        \
+      ++failures;                              \
+    }                                          \
+  } while (0)
+
+static int body_slots(int vpl, int nslot) {  // the kernel's dispatch: VPL, VPL/2, ...
+  int v = vpl;
+  while (v > 1 && nslot <= v / 2) v /= 2;
+  return v;
+}
+
+static void check_seg(const qkn::Seg& s, int nw, int vpl, int64_t nvec, int K, bool masked, const char* what) {
+  const int wl = s.wpr_log2, m = s.sub_log2;
+  CHECK(m >= 0 && m <= wl, "%s sub_log2 %d wpr_log2 %d", what, m, wl);
+  CHECK(s.nslot >= 1 && s.nslot <= vpl, "%s nslot %d vpl %d", what, s.nslot, vpl);
+  CHECK(s.rows_per_wg * (1 << wl) == nw, "%s rows_per_wg", what);
+  CHECK(static_cast<int64_t>(s.row_bytes) == nvec * 16, "%s row_bytes", what);
+  const int lanes = 64 << wl;
+  const int nsub = 1 << (wl - m);
+  const int64_t sv = s.slice_vec;
+  std::vector<int> count(nvec, 0);
+  // slice held by (sub-team, slot); -2 = unset, -1 = empty for this sub-team
+  std::vector<std::vector<int>> slot_slice(nsub, std::vector<int>(s.nslot, -2));
+  for (int tl = 0; tl < lanes; ++tl) {
+    const int sub = (tl >> 6) >> m;
+    for (int j = 0; j < s.nslot; ++j) {
+      const int v = qkn::slot_vector(s.slot_lim[j], s.slot_base[j], tl, wl, m, s.slice_vec, s.lay_k);
+      if (v < 0) continue;
+      CHECK(v < nvec, "%s vector %d >= %lld", what, v, (long long)nvec);
+      if (v >= nvec) continue;
+      ++count[v];
+      const int sl = static_cast<int>(v / sv);
+      if (!masked) {
+        int& rec = slot_slice[sub][j];
+        CHECK(rec == -2 || rec == sl, "%s slot %d mixes slices %d and %d", what, j, rec, sl);
+        rec = sl;
+      }
+    }
+  }
+  for (int64_t v = 0; v < nvec; ++v) CHECK(count[v] == 1, "%s vector %lld held %d times", what, (long long)v, count[v]);
+  for (int j = s.nslot; j < qkn::kMaxSlots; ++j) CHECK(s.slot_lim[j] == 0, "%s unused slot %d not empty", what, j);
+  if (!masked) {
+    for (int u = 0; u < nsub; ++u) {
+      int flushes = 0;
+      for (int j = 0; j < s.nslot; ++j) {
+        const bool flush = (s.flush_mask >> j) & 1u;
+        const int sl = slot_slice[u][j];
+        const int next = j + 1 < s.nslot ? slot_slice[u][j + 1] : -3;
+        const int expect = u + flushes * nsub;  // the slice the kernel's partial counter stands at
+        if (sl >= 0) {
+          CHECK(sl == expect, "%s sub %d slot %d holds slice %d, counter at %d", what, u, j, sl, expect);
+          CHECK(flush == (next != sl), "%s sub %d slot %d flush bit %d", what, u, j, (int)flush);
+        }
+        if (flush) ++flushes;
+      }
+      CHECK(flushes <= 64, "%s too many partials", what);
+    }
+  }
+  if (s.lds_gamma) {
+    const int v = body_slots(vpl, s.nslot);
+    CHECK(nvec <= static_cast<int64_t>((v + 1) / 2) * nw * 64, "%s staged gamma exceeds the copy loop", what);
+    CHECK(s.rows_per_wg > 1, "%s staged gamma with one row per workgroup", what);
+  }
+}
+
+static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr, int dtype) {
+  qknorm_ctx ctx{0, 256, qknorm_options{forced_wpr, 0, 0}};
+  const int64_t ve = vec_elems(dtype);
+  SegIn in[2] = {{hq / ve, K}, {hk / ve, K}};
+  const int nseg = hk > 0 ? 2 : 1;
+  Plan plans[2];
+  int nw = 4;
+  const int st = plan_launch(&ctx, in, nseg, T, plans, &nw);
+  if (st != QKNORM_OK) {
+    // only a pinned team that cannot hold the row may be refused
+    CHECK(forced_wpr != 0, "auto plan refused T=%lld hq=%lld hk=%lld K=%d", (long long)T, (long long)hq,
+          (long long)hk, K);
+    return;
+  }
+  bool masked = false;
+  for (int i = 0; i < nseg; ++i) masked = masked || plans[i].masked;
+  int slots = 0;
+  qkn::Seg seg[2];
+  for (int i = 0; i < nseg; ++i) {
+    Plan pl = plans[i];
+    if (masked && !pl.masked) pl = Plan{pl.wpr_log2, pl.wpr_log2, plain_slots(in[i].nvec, pl.wpr_log2), true};
+    fill_layout(&seg[i], pl, nw, in[i].nvec, K, T);
+    share_gamma(&seg[i]);
+    slots = seg[i].nslot > slots ? seg[i].nslot : slots;
+  }
+  const int vpl = qkn::compiled_vpl(slots, nw);
+  char what[160];
+  std::snprintf(what, sizeof what, "T=%lld hq=%lld hk=%lld K=%d wpr=%d dt=%d", (long long)T, (long long)hq,
+                (long long)hk, K, forced_wpr, dtype);
+  CHECK(vpl > 0, "%s no compiled variant for %d slots", what, slots);
+  if (vpl == 0) return;
+  for (int i = 0; i < nseg; ++i) check_seg(seg[i], nw, vpl, in[i].nvec, K, masked, what);
+}
+
+int main() {
+  int cases = 0;
+  const int64_t widths[] = {8, 24, 64, 96, 200, 256, 512, 1000, 1024, 1032, 1280, 1536, 2048,
+                            4096, 5120, 8192, 12288, 16384, 32768, 65536};
+  const int64_t rows[] = {1, 3, 64, 256, 2048, 16384};
+  const int ks[] = {1, 2, 3, 4, 5, 8, 10, 16, 24, 32, 40, 48, 64};
+  const int wprs[] = {0, 1, 2, 4, 8, 16};
+  for (int dtype : {QKNORM_BF16, QKNORM_F32})
+    for (int64_t hq : widths)
+      for (int K : ks) {
+        const int64_t ve = vec_elems(dtype);
+        if (hq > qknorm_max_width(dtype) || hq % K || (hq / K) % ve) continue;
+        for (int64_t T : rows)
+          for (int w : wprs) {
+            run_forward(T, hq, 0, K, w, dtype);
+            ++cases;
+            // a key segment of a quarter / the same width, when it slices evenly
+            for (int64_t hk : {hq / 4, hq}) {
+              if (hk < ve || hk % K || (hk / K) % ve) continue;
+              run_forward(T, hq, hk, K, w, dtype);
+              ++cases;
+            }
+          }
+      }
+  std::printf("%d cases, %d failures\n", cases, failures);
+  return failures ? 1 : 0;
+}
