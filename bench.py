@@ -104,10 +104,74 @@ def cpu_baseline(d, num_slices, seconds):
     for _ in range(reps):
         oracle.qk_forward(qs[:rows], ks[:rows], gq, gk, w.eps, num_slices)
     total = time.perf_counter() - t0
+    # the same oracle on one thread, over a smaller sample (about a fifth of the time)
     oracle.set_threads(1)
+    rows1 = max(1, min(rows, int(rows * reps * (seconds / 5.0) / (cores * seconds))))
+    t0 = time.perf_counter()
+    oracle.qk_forward(qs[:rows1], ks[:rows1], gq, gk, w.eps, num_slices)
+    one = time.perf_counter() - t0
     return {"value": rows * reps / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "%d of %d tokens (q %d + k %d columns, %s), K=%d, %d passes in %.1f s" % (
-                rows, w.T, w.hq, w.hk, w.dtype, num_slices, reps, total)}
+                rows, w.T, w.hq, w.hk, w.dtype, num_slices, reps, total),
+            "one_thread": {"value": rows1 / one, "unit": "tokens/s", "sample": "%d tokens, %.1f s" % (rows1, one)},
+            "host_cpus": os.cpu_count()}
+
+
+def split_path(torch, qk, w, sets, gq, gk, ctx, stream, timed, K, args):
+    """The split entry points over the workload's rows. Two readings:
+    the whole computation on this GPU (every slice's partial_stats, then every
+    slice's apply_stats, for q and k), and one tensor-parallel rank's share
+    (slice 0 of q and of k: its partial sums, then its normalisation with all
+    K partials). Bytes count what each call must move: x read by both calls,
+    y written once, gamma once, and the partial sums written and read."""
+    dev = gq.device
+    eb = w.elem_bytes
+    stats = (torch.zeros((K, w.T), dtype=torch.float32, device=dev),
+             torch.zeros((K, w.T), dtype=torch.float32, device=dev))
+    views = []
+    for q, k, yq, yk in sets:
+        per = []
+        for x, y, g, st, H in ((q, yq, gq, stats[0], w.hq), (k, yk, gk, stats[1], w.hk)):
+            ws = H // K
+            per.append([(x[:, s * ws:(s + 1) * ws], y[:, s * ws:(s + 1) * ws], g[s * ws:(s + 1) * ws], st, H, s)
+                        for s in range(K)])
+        views.append(per)
+
+    def stats_of(sl):
+        for xs, _, _, st, _, s in sl:
+            qk.partial_stats(xs, s, K, stats=st, ctx=ctx, stream=stream)
+
+    def apply_of(sl):
+        for xs, ys, gs, st, H, _ in sl:
+            qk.apply_stats(xs, gs, st, H, eps=w.eps, out=ys, ctx=ctx, stream=stream)
+
+    def whole(i):
+        for sl in views[i % len(views)]:
+            stats_of(sl)
+        for sl in views[i % len(views)]:
+            apply_of(sl)
+
+    def rank(i):
+        per = views[i % len(views)]
+        for sl in per:
+            stats_of(sl[:1])
+        for sl in per:
+            apply_of(sl[:1])
+
+    n = max(10, min(args.steps, 50))
+    for i in range(5):
+        whole(i)
+    whole_ms = timed(n, whole, launches=4 * K)[0]
+    rank_ms = timed(n, rank, launches=4)[0]
+    H2 = w.hq + w.hk
+    whole_bytes = 3 * w.T * H2 * eb + H2 * eb + 2 * (K * w.T * 4 + K * K * w.T * 4)
+    rank_bytes = 3 * w.T * H2 // K * eb + H2 // K * eb + 2 * (w.T * 4 + K * w.T * 4)
+    return {"split_path": {
+        "num_slices": K,
+        "whole_us": whole_ms * 1e3, "whole_launches": 4 * K, "whole_bytes": whole_bytes,
+        "whole_gbs": whole_bytes / (whole_ms * 1e-3) / 1e9,
+        "rank_share_us": rank_ms * 1e3, "rank_share_launches": 4, "rank_share_bytes": rank_bytes,
+        "rank_share_gbs": rank_bytes / (rank_ms * 1e-3) / 1e9}}
 
 
 def main():
@@ -182,10 +246,10 @@ def main():
     # kernels, not the host's launch rate.
     cyc_per_us = calibrate_sleep(torch, stream)
 
-    def timed(n, fn):
+    def timed(n, fn, launches=1):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        torch.cuda._sleep(int(cyc_per_us * (200.0 + 40.0 * n)))
+        torch.cuda._sleep(int(cyc_per_us * (200.0 + 40.0 * n * launches)))
         e0.record(stream)
         h0 = time.perf_counter()
         for i in range(n):
@@ -227,6 +291,21 @@ def main():
         t_.copy_(s_)
     copy_ms = timed(args.steps, lambda i: cbufs[i % csets][1].copy_(cbufs[i % csets][0]))[0]
     del cbufs
+
+    # host view of one call: enqueue, then wait for completion (decode latency)
+    lat = []
+    for i in range(min(args.steps, 200)):
+        t0 = time.perf_counter()
+        step(i)
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - t0) * 1e6)
+    lat.sort()
+    extra["host_call_to_done_us_p10_p50_p90"] = [lat[len(lat) // 10], lat[len(lat) // 2],
+                                                  lat[(9 * len(lat)) // 10]]
+
+    # the split path (partial statistics, then apply) over the same rows
+    if max(w.slices) > 1:
+        extra.update(split_path(torch, qk, w, sets, gq, gk, ctx, stream, timed, max(w.slices), args))
 
     achieved_gbs = algo_bytes / (kern_ms * 1e-3) / 1e9
     traffic = None

@@ -39,6 +39,8 @@ def load(path):
     L.oracle_forward.argtypes = [_fp, i64, i64, i64, _fp, ctypes.c_double,
                                  ctypes.c_int, _dp, _dp, i64]
     L.oracle_forward.restype = None
+    L.oracle_headwise.argtypes = [_fp, i64, i64, i64, i64, _fp, ctypes.c_double, _dp, i64]
+    L.oracle_headwise.restype = None
     return L
 
 
@@ -168,3 +170,30 @@ def qk_forward(q, k, gamma_q, gamma_k, eps, num_slices=1):
     yq, _ = forward(q, gamma_q, eps, num_slices)
     yk, _ = forward(k, gamma_k, eps, num_slices)
     return yq, yk
+
+
+def headwise(x, gamma, head_dim, eps):
+    """Headwise RMSNorm (review, "Layerwise vs. headwise QK-Norm"): every
+    head of `head_dim` contiguous columns is normalised with its own
+    statistic, and the `head_dim` weights of gamma are shared by all heads.
+
+    x: [T, H] with H a multiple of head_dim; gamma: [head_dim].
+    Returns y float64 [T, H]."""
+    x = _rows(x)
+    T, H = x.shape
+    D = int(head_dim)
+    if D < 1 or H % D:
+        raise ValueError("width %d is not a whole number of %d-column heads" % (H, D))
+    g = as_f32(gamma).reshape(-1)
+    if g.shape[0] != D:
+        raise ValueError("gamma must have head_dim weights")
+    y = np.empty((T, H), dtype=np.float64)
+    lib().oracle_headwise(x.ctypes.data_as(_fp), T, H, H, D, g.ctypes.data_as(_fp),
+                          eps_as_gpu_sees_it(eps), y.ctypes.data_as(_dp), H)
+    return y
+
+
+def qk_headwise(q, k, gamma_q, gamma_k, head_dim, eps):
+    """Headwise QK-Norm of the query rows and the key rows, each tensor with
+    its own head_dim-long weights. Returns (y_q, y_k) in float64."""
+    return headwise(q, gamma_q, head_dim, eps), headwise(k, gamma_k, head_dim, eps)

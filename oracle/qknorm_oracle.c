@@ -111,3 +111,36 @@ void oracle_forward(const float *x, int64_t T, int64_t H, int64_t ldx,
     oracle_slice_sumsq(x, T, H, ldx, K, P);
     oracle_apply(x, T, H, ldx, P, K, gamma, H, eps, y, ldy);
 }
+
+/*
+ * Headwise QK-Norm (review, "Layerwise vs. headwise QK-Norm": one
+ * normalisation factor per attention head instead of one per projected
+ * row). Each row's H columns hold H / D heads of D contiguous columns, head
+ * 0 first. Head h uses only its own columns: its sum of squares (ascending
+ * column order), its mean over D, eps inside the square root as in Eq. 1,
+ * and the D weights of gamma, which every head shares.
+ *   x     : T rows of H columns (row t at x + t*ldx); H % D == 0
+ *   gamma : D weights
+ *   y     : out, T rows of H doubles, row t at y + t*ldy
+ */
+void oracle_headwise(const float *x, int64_t T, int64_t H, int64_t ldx,
+                     int64_t D, const float *gamma, double eps,
+                     double *y, int64_t ldy)
+{
+    int64_t t;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (t = 0; t < T; ++t) {
+        const float *row = x + t * ldx;
+        double *out = y + t * ldy;
+        for (int64_t h0 = 0; h0 < H; h0 += D) {
+            double S = 0.0;
+            for (int64_t j = 0; j < D; ++j) {
+                const double v = (double)row[h0 + j];
+                S += v * v;
+            }
+            const double rms = sqrt(S / (double)D + eps);
+            for (int64_t j = 0; j < D; ++j)
+                out[h0 + j] = (double)row[h0 + j] / rms * (double)gamma[j];
+        }
+    }
+}

@@ -228,6 +228,74 @@ def pin_library_rms_norm():
             np.testing.assert_allclose(y, ref, rtol=1e-14, atol=0)
 
 
+def pin_headwise_closed_form():
+    """Headwise statistics on the worked example's row (H = 8) cut into two
+    heads of 4: the first head's sum of squares is 6.25, so with eps = 0 its
+    RMS is exactly 1.25; the second head's is 15.5 (mean 3.875). Each head is
+    normalised by its own statistic, and the 4 weights apply to both heads."""
+    x = _ex([1.0, 2.0, -1.0, 0.5, 3.0, -2.0, 1.5, 0.5])
+    g = np.asarray([1.0, 0.5, 2.0, 4.0], F32)
+    y = oracle.headwise(x, np.ones(4, F32), 4, 0.0)
+    np.testing.assert_allclose(y[0, :4], [0.8, 1.6, -0.8, 0.4], rtol=1e-15, atol=0)
+    r1 = 1.0 / math.sqrt(3.875)
+    np.testing.assert_allclose(y[0, 4:], [3.0 * r1, -2.0 * r1, 1.5 * r1, 0.5 * r1], rtol=2e-16, atol=0)
+    y = oracle.headwise(x, g, 4, 0.0)
+    np.testing.assert_allclose(y[0, :4], [0.8, 0.8, -1.6, 1.6], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(y[0, 4:], [3.0 * r1, -1.0 * r1, 3.0 * r1, 2.0 * r1], rtol=2e-16, atol=0)
+    # eps joins each head's own mean inside the root
+    eps = oracle.eps_as_gpu_sees_it(1e-6)
+    y = oracle.headwise(x, np.ones(4, F32), 4, 1e-6)
+    np.testing.assert_allclose(y[0, :4], x[0, :4].astype(np.float64) / math.sqrt(1.5625 + eps), rtol=2e-16)
+    np.testing.assert_allclose(y[0, 4:], x[0, 4:].astype(np.float64) / math.sqrt(3.875 + eps), rtol=2e-16)
+    # heads of 2: sums 5, 1.25, 13, 2.5 (means 2.5, 0.625, 6.5, 1.25)
+    y = oracle.headwise(x, np.ones(2, F32), 2, 0.0)
+    for h, m in enumerate((2.5, 0.625, 6.5, 1.25)):
+        np.testing.assert_allclose(y[0, 2 * h:2 * h + 2],
+                                   x[0, 2 * h:2 * h + 2].astype(np.float64) / math.sqrt(m), rtol=2e-16)
+
+
+def pin_headwise_exact_rows():
+    """Distinct rows and heads against exact arithmetic, head by head, with
+    the shared weights: catches head-offset, weight-index and stride mistakes."""
+    T, D, nh = 3, 8, 4
+    x = workloads.random_rows(T, D * nh, "f32", 71).numpy()
+    g = workloads.random_weights(D, "f32", 72).numpy()
+    eps = oracle.eps_as_gpu_sees_it(1e-6)
+    y = oracle.headwise(x, g, D, eps)
+    for t in range(T):
+        for h in range(nh):
+            ref = [float(v) for v in exact.rmsnorm_row(x[t, h * D:(h + 1) * D], g, eps)]
+            np.testing.assert_allclose(y[t, h * D:(h + 1) * D], ref, rtol=1e-15, atol=0)
+
+
+def pin_headwise_reductions():
+    """One head spanning the row is the layerwise norm; heads are independent
+    of each other; torch's rms_norm over the rows reshaped to one head per row
+    (float64) is an independent library implementation."""
+    eps = oracle.eps_as_gpu_sees_it(1e-6)
+    x = workloads.random_rows(5, 512, "f32", 81).numpy()
+    g = workloads.random_weights(512, "f32", 82).numpy()
+    y1, _ = oracle.forward(x, g, eps, 1)
+    assert np.array_equal(oracle.headwise(x, g, 512, eps), y1)
+    D = 128
+    gh = workloads.random_weights(D, "f32", 83).numpy()
+    y = oracle.headwise(x, gh, D, eps)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x).double().reshape(-1, D), (D,),
+                                       torch.from_numpy(gh).double(), eps).reshape(5, 512).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=0)
+    # scaling head 2 changes head 2 only; with eps = 0 not even head 2
+    x2 = x.copy()
+    x2[:, 2 * D:3 * D] *= F32(4)
+    y2 = oracle.headwise(x2, gh, D, eps)
+    keep = np.r_[0:2 * D, 3 * D:4 * D]
+    assert np.array_equal(y2[:, keep], y[:, keep])
+    assert not np.array_equal(y2[:, 2 * D:3 * D], y[:, 2 * D:3 * D])
+    assert np.array_equal(oracle.headwise(x2, gh, D, 0.0), oracle.headwise(x, gh, D, 0.0))
+    # unit mean square per head when the weights are 1 and eps = 0
+    y0 = oracle.headwise(x, np.ones(D, F32), D, 0.0).reshape(5, 4, D)
+    np.testing.assert_allclose((y0 * y0).mean(axis=2), 1.0, rtol=1e-13)
+
+
 ALL_PINS = [
     pin_worked_example_printed,
     pin_worked_example_exact,
@@ -239,4 +307,7 @@ ALL_PINS = [
     pin_special_cases,
     pin_brute_force_rows,
     pin_library_rms_norm,
+    pin_headwise_closed_form,
+    pin_headwise_exact_rows,
+    pin_headwise_reductions,
 ]

@@ -16,11 +16,18 @@ MUTANTS = [
     ("dropped_last_term", "j < (s + 1) * w;", "j < (s + 1) * w - 1;"),
     ("slices_reversed", "P[(int64_t)s * T + t] = acc;", "P[(int64_t)(K - 1 - s) * T + t] = acc;"),
     ("row_stride_ignored", "const float *row = x + t * ldx;\n        for (int s", "const float *row = x + t;\n        for (int s"),
-    ("gamma_reversed", "(double)gamma[j]", "(double)gamma[W - 1 - j]"),
+    ("gamma_reversed", "* (double)gamma[j]; /* Eq. 1 order */", "* (double)gamma[W - 1 - j];"),
     ("multiply_by_rms", "(double)row[j] / rms", "(double)row[j] * rms"),
     ("output_sign", "out[j] = (double)row[j]", "out[j] = -(double)row[j]"),
     ("abs_not_square", "acc += v * v;", "acc += v < 0 ? -v : v;"),
     ("first_slice_only", "for (int s = 0; s < K; ++s) /* Eq. 5", "for (int s = 0; s < 1; ++s) /* Eq. 5"),
+    # headwise
+    ("head_mean_over_row", "sqrt(S / (double)D + eps)", "sqrt(S / (double)H + eps)"),
+    ("head_eps_outside_sqrt", "sqrt(S / (double)D + eps)", "(sqrt(S / (double)D) + eps)"),
+    ("head_stat_of_first_head", "const double v = (double)row[h0 + j];", "const double v = (double)row[j];"),
+    ("head_dropped_last_term", "for (int64_t j = 0; j < D; ++j) {", "for (int64_t j = 0; j < D - 1; ++j) {"),
+    ("head_weights_shifted", "/ rms * (double)gamma[j];\n        }", "/ rms * (double)gamma[(j + 1) % D];\n        }"),
+    ("head_weights_by_column", "/ rms * (double)gamma[j];\n        }", "/ rms * (double)gamma[(j + (h0 > 0)) % D];\n        }"),
 ]
 
 
