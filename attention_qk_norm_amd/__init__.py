@@ -27,8 +27,8 @@ ERR_NULL, ERR_SHAPE, ERR_SLICES, ERR_ALIGN, ERR_DTYPE, ERR_EPS, ERR_ALIAS, ERR_D
 
 # Every symbol include/qknorm.h declares.
 EXPORTS = ("qknorm_create", "qknorm_create_ex", "qknorm_destroy", "qknorm_forward",
-           "qknorm_partial_stats", "qknorm_apply_stats", "qknorm_status_string",
-           "qknorm_max_width")
+           "qknorm_forward_headwise", "qknorm_partial_stats", "qknorm_apply_stats",
+           "qknorm_status_string", "qknorm_max_width")
 
 
 class Rows(ctypes.Structure):
@@ -69,6 +69,8 @@ def lib():
             L.qknorm_destroy.argtypes = [vp]
             L.qknorm_forward.argtypes = [vp, ci, i64, ctypes.POINTER(Rows), ctypes.POINTER(Rows),
                                          vp, vp, cf, ci, vp]
+            L.qknorm_forward_headwise.argtypes = [vp, ci, i64, ctypes.POINTER(Rows), ctypes.POINTER(Rows),
+                                                  vp, vp, i64, cf, vp]
             L.qknorm_partial_stats.argtypes = [vp, ci, i64, vp, i64, i64, ci, ci, vp, vp]
             L.qknorm_apply_stats.argtypes = [vp, ci, i64, ctypes.POINTER(Rows), vp, vp, ci, i64,
                                              cf, vp]
@@ -77,7 +79,7 @@ def lib():
             L.qknorm_max_width.argtypes = [ci]
             L.qknorm_max_width.restype = i64
             for name in ("qknorm_create", "qknorm_create_ex", "qknorm_destroy", "qknorm_forward",
-                         "qknorm_partial_stats", "qknorm_apply_stats"):
+                         "qknorm_forward_headwise", "qknorm_partial_stats", "qknorm_apply_stats"):
                 getattr(L, name).restype = ci
             _lib = L
         return _lib
@@ -168,12 +170,9 @@ def _ctx_of(t, ctx):
     return ctx if ctx is not None else default_context(t.device.index or 0)
 
 
-def forward(q, k, gamma_q, gamma_k, eps=1e-6, num_slices=1, out_q=None, out_k=None,
-            ctx=None, stream=None):
-    """Layerwise QK-Norm of q [T, Hq] and k [T, Hk] (k may be None) in one launch.
-
-    Outputs are new tensors unless out_q / out_k are given; passing the input
-    itself (out_q=q) normalises in place. Returns (y_q, y_k)."""
+def _qk_rows(q, k, gamma_q, gamma_k, gamma_width, out_q, out_k):
+    """Marshal the query and key tensors of a fused call: (dtype, T, rows of q,
+    rows of k or None, y_q, y_k). gamma_width(x) is the weight count for rows x."""
     torch = _torch()
     dt = _dtype_code(q)
     T = q.shape[0]
@@ -192,14 +191,41 @@ def forward(q, k, gamma_q, gamma_k, eps=1e-6, num_slices=1, out_q=None, out_k=No
     for g, x in ((gamma_q, q), (gamma_k, k)):
         if x is None:
             continue
-        if g.dtype != x.dtype or g.dim() != 1 or g.shape[0] != x.shape[1] or not g.is_contiguous():
-            raise ValueError("gamma must be a contiguous 1-D tensor of the rows' dtype and width")
+        if g.dtype != x.dtype or g.dim() != 1 or g.shape[0] != gamma_width(x) or not g.is_contiguous():
+            raise ValueError("gamma must be a contiguous 1-D tensor of the rows' dtype with %d weights"
+                             % gamma_width(x))
+    return dt, T, rq, rk, out_q, out_k
+
+
+def forward(q, k, gamma_q, gamma_k, eps=1e-6, num_slices=1, out_q=None, out_k=None,
+            ctx=None, stream=None):
+    """Layerwise QK-Norm of q [T, Hq] and k [T, Hk] (k may be None) in one launch.
+
+    Outputs are new tensors unless out_q / out_k are given; passing the input
+    itself (out_q=q) normalises in place. Returns (y_q, y_k)."""
+    dt, T, rq, rk, out_q, out_k = _qk_rows(q, k, gamma_q, gamma_k, lambda x: x.shape[1], out_q, out_k)
     c = _ctx_of(q, ctx)
     st = lib().qknorm_forward(c.handle, dt, T, ctypes.byref(rq),
                               ctypes.byref(rk) if rk is not None else None,
                               gamma_q.data_ptr(), gamma_k.data_ptr() if k is not None else None,
                               float(eps), int(num_slices), _stream_of(q, stream))
     _check(st, "qknorm_forward")
+    return out_q, out_k
+
+
+def forward_headwise(q, k, gamma_q, gamma_k, head_dim, eps=1e-6, out_q=None, out_k=None,
+                     ctx=None, stream=None):
+    """Headwise QK-Norm of q [T, Hq] and k [T, Hk] (k may be None) in one
+    launch: every head of `head_dim` columns has its own statistic, and
+    gamma_q / gamma_k hold `head_dim` weights shared by the heads of their
+    tensor. Outputs as for forward(). Returns (y_q, y_k)."""
+    dt, T, rq, rk, out_q, out_k = _qk_rows(q, k, gamma_q, gamma_k, lambda x: int(head_dim), out_q, out_k)
+    c = _ctx_of(q, ctx)
+    st = lib().qknorm_forward_headwise(c.handle, dt, T, ctypes.byref(rq),
+                                       ctypes.byref(rk) if rk is not None else None,
+                                       gamma_q.data_ptr(), gamma_k.data_ptr() if k is not None else None,
+                                       int(head_dim), float(eps), _stream_of(q, stream))
+    _check(st, "qknorm_forward_headwise")
     return out_q, out_k
 
 

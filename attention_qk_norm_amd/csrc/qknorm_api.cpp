@@ -106,6 +106,49 @@ int check_ctx(const qknorm_ctx* ctx) {
   return QKNORM_OK;
 }
 
+// Vectors per head when `head_dim` columns make a valid head (a power of two
+// of 16-byte vectors, at most one wavefront's 64), else 0.
+int head_vectors(int64_t head_dim, int dtype) {
+  const int64_t bytes = head_dim * elem_bytes(dtype);
+  if (head_dim < 1 || bytes % kVecBytes != 0) return 0;
+  const int64_t hv = bytes / kVecBytes;
+  return (hv <= 64 && (hv & (hv - 1)) == 0) ? static_cast<int>(hv) : 0;
+}
+
+// Validation shared by the two fused calls, after dtype and T: each tensor's
+// pointers, shape and alignment, its cut (num_slices equal slices, or heads
+// of head_dim columns when `headwise`), eps, then aliasing. gamma has
+// `width` weights (layerwise) or `head_dim` (headwise).
+int check_fused(int dtype, int64_t T, const qknorm_rows* const* segs, const void* const* gammas, int nseg,
+                int num_slices, bool headwise, int64_t head_dim, float eps) {
+  const int64_t ve = vec_elems(dtype);
+  for (int i = 0; i < nseg; ++i) {
+    const int st = check_rows(segs[i], gammas[i], dtype, true, true);
+    if (st != QKNORM_OK) return st;
+    if (segs[i]->width > qknorm_max_width(dtype)) return QKNORM_ERR_SHAPE;
+    if (headwise) {
+      if (head_vectors(head_dim, dtype) == 0 || segs[i]->width % head_dim != 0) return QKNORM_ERR_SLICES;
+    } else if (num_slices < 1 || num_slices > kMaxSlices || segs[i]->width % num_slices != 0 ||
+               (segs[i]->width / num_slices) % ve != 0) {
+      return QKNORM_ERR_SLICES;
+    }
+  }
+  if (!eps_ok(eps)) return QKNORM_ERR_EPS;
+  const int eb = elem_bytes(dtype);
+  for (int i = 0; i < nseg; ++i) {
+    if (!in_out_ok(*segs[i], dtype, T)) return QKNORM_ERR_ALIAS;
+    const Rows yi = out_rows(*segs[i], dtype, T);
+    for (int j = 0; j < nseg; ++j) {
+      const int64_t gw = headwise ? head_dim : segs[j]->width;
+      if (overlap(yi, flat(gammas[j], gw * eb))) return QKNORM_ERR_ALIAS;
+      if (j == i) continue;
+      if (overlap(yi, in_rows(*segs[j], dtype, T)) || overlap(yi, out_rows(*segs[j], dtype, T)))
+        return QKNORM_ERR_ALIAS;
+    }
+  }
+  return QKNORM_OK;
+}
+
 // How one segment's rows are spread over lanes.
 struct Plan {
   int wpr_log2 = 0;  // team: 2^wpr_log2 wavefronts per row
@@ -382,27 +425,9 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
   const void* gammas[2] = {gamma_q, gamma_k};
   const int nseg = k != nullptr ? 2 : 1;
   const int64_t ve = vec_elems(dtype);
-  for (int i = 0; i < nseg; ++i) {
-    const int st = check_rows(segs[i], gammas[i], dtype, true, true);
-    if (st != QKNORM_OK) return st;
-    if (segs[i]->width > qknorm_max_width(dtype)) return QKNORM_ERR_SHAPE;
-    if (num_slices < 1 || num_slices > kMaxSlices || segs[i]->width % num_slices != 0 ||
-        (segs[i]->width / num_slices) % ve != 0)
-      return QKNORM_ERR_SLICES;
-  }
-  if (!eps_ok(eps)) return QKNORM_ERR_EPS;
-  const int eb = elem_bytes(dtype);
-  for (int i = 0; i < nseg; ++i) {
-    if (!in_out_ok(*segs[i], dtype, T)) return QKNORM_ERR_ALIAS;
-    const Rows yi = out_rows(*segs[i], dtype, T);
-    for (int j = 0; j < nseg; ++j) {
-      if (overlap(yi, flat(gammas[j], segs[j]->width * eb))) return QKNORM_ERR_ALIAS;
-      if (j == i) continue;
-      if (overlap(yi, in_rows(*segs[j], dtype, T)) || overlap(yi, out_rows(*segs[j], dtype, T)))
-        return QKNORM_ERR_ALIAS;
-    }
-  }
-  int st = check_ctx(ctx);
+  int st = check_fused(dtype, T, segs, gammas, nseg, num_slices, false, 0, eps);
+  if (st != QKNORM_OK) return st;
+  st = check_ctx(ctx);
   if (st != QKNORM_OK) return st;
 
   SegIn in[2];
@@ -437,6 +462,54 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
   }
   qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw), nw, masked,
                  ctx->opt.cached_rows == 0 || masked, false};
+  if (v.vpl == 0) return QKNORM_ERR_SHAPE;
+  return run(ctx, v, a, nseg, stream);
+}
+
+int qknorm_forward_headwise(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, const qknorm_rows* k,
+                            const void* gamma_q, const void* gamma_k, int64_t head_dim, float eps,
+                            void* stream) {
+  if (!valid_dtype(dtype)) return QKNORM_ERR_DTYPE;
+  if (T < 0 || T > kMaxRows) return QKNORM_ERR_SHAPE;
+  if (T == 0) return QKNORM_OK;
+  const qknorm_rows* segs[2] = {q, k};
+  const void* gammas[2] = {gamma_q, gamma_k};
+  const int nseg = k != nullptr ? 2 : 1;
+  int st = check_fused(dtype, T, segs, gammas, nseg, 1, true, head_dim, eps);
+  if (st != QKNORM_OK) return st;
+  st = check_ctx(ctx);
+  if (st != QKNORM_OK) return st;
+
+  const int64_t ve = vec_elems(dtype);
+  SegIn in[2];
+  for (int i = 0; i < nseg; ++i) in[i] = SegIn{segs[i]->width / ve, 1};
+  Plan plans[2];
+  int nw = 4;
+  st = plan_launch(ctx, in, nseg, T, plans, &nw);
+  if (st != QKNORM_OK) return st;
+  const int hv = head_vectors(head_dim, dtype);
+  int hl = 0;
+  while ((1 << hl) < hv) ++hl;
+  qkn::Args a{};
+  a.T = T;
+  a.eps = eps;
+  int slots = 0;
+  for (int i = 0; i < nseg; ++i) {
+    // one slice is never masked: heads rely on the strided layout
+    if (plans[i].masked) return QKNORM_ERR_SHAPE;
+    qkn::Seg& s = a.seg[i];
+    s.x = segs[i]->x;
+    s.y = segs[i]->y;
+    s.gamma = gammas[i];
+    s.x_stride = segs[i]->x_stride;
+    s.y_stride = segs[i]->y_stride;
+    fill_layout(&s, plans[i], nw, in[i].nvec, 1, T);
+    s.head_log2 = hl;
+    s.h = static_cast<float>(head_dim);
+    s.inv_h = 1.0f / static_cast<float>(head_dim);
+    slots = s.nslot > slots ? s.nslot : slots;
+  }
+  qkn::Variant v{dtype, qkn::MODE_HEAD, qkn::compiled_vpl(slots, nw), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, nseg, stream);
 }

@@ -147,16 +147,17 @@ struct Hot {
   const float* stats_in;
   float* stats_out;
   int64_t x_stride, y_stride, T;
-  int rows_per_wg, nwg, nslot, wpr_log2, sub_log2, lds_gamma, lay_k, comb_k, slice_vec;
+  int rows_per_wg, nwg, nslot, wpr_log2, sub_log2, lds_gamma, lay_k, comb_k, slice_vec, head_log2;
   uint32_t row_bytes, flush_mask;
-  float inv_slice_vec, h, eps;
+  float inv_slice_vec, h, inv_h, eps;
 
   __device__ __forceinline__ Hot(const Args& a, const Seg& s)
       : x(s.x), y(s.y), gamma(s.gamma), stats_in(s.stats_in), stats_out(s.stats_out),
         x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
         nslot(s.nslot), wpr_log2(s.wpr_log2), sub_log2(s.sub_log2), lds_gamma(s.lds_gamma),
-        lay_k(s.lay_k), comb_k(s.comb_k), slice_vec(s.slice_vec), row_bytes(s.row_bytes),
-        flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h), eps(a.eps) {}
+        lay_k(s.lay_k), comb_k(s.comb_k), slice_vec(s.slice_vec), head_log2(s.head_log2),
+        row_bytes(s.row_bytes), flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h),
+        inv_h(s.inv_h), eps(a.eps) {}
 };
 
 // The segment's slot table, read at kernel entry with the other arguments.
@@ -311,6 +312,62 @@ __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const u32x4 (&
   }
 }
 
+// Headwise (review, "Layerwise vs. headwise QK-Norm"): sums over aligned
+// groups of 2^hl lanes (hl <= 6), one group per head, every lane of a group
+// receiving the same value. Within a row of 16 lanes each butterfly step
+// adds the partner group's sum, and the addition is commutative, so the
+// lanes agree bit for bit; groups of 32 and 64 lanes add the row sums read
+// from lanes 0, 16, 32 and 48 in a fixed order.
+template <int V>
+__device__ __forceinline__ void head_sums(float (&q)[V], int hl, int lane) {
+  if (hl >= 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) q[j] += dpp<0xB1>(q[j]);
+  }
+  if (hl >= 2) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) q[j] += dpp<0x4E>(q[j]);
+  }
+  if (hl >= 3) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) q[j] += dpp<0x141>(q[j]);
+  }
+  if (hl >= 4) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) q[j] += dpp<0x140>(q[j]);
+  }
+  if (hl == 5) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const float lo = lane_value(q[j], 0) + lane_value(q[j], 16);
+      const float hi = lane_value(q[j], 32) + lane_value(q[j], 48);
+      q[j] = lane < 32 ? lo : hi;
+    }
+  } else if (hl == 6) {
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      q[j] = (lane_value(q[j], 0) + lane_value(q[j], 16)) + (lane_value(q[j], 32) + lane_value(q[j], 48));
+  }
+}
+
+// One row, headwise: each slot's head statistic, then its own inverse RMS
+// (the mean divides by the head width) and the head's weights `g`, which
+// are the same vector for every slot of this lane.
+template <class E, int VPL, bool NT>
+__device__ __forceinline__ void head_finish(const u32x4 (&d)[VPL], u32x4 g, const Hot& s,
+                                            const Layout<VPL>& L, int64_t row, bool live, int lane) {
+  float q[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) q[j] = E::sumsq(d[j], 0.f);
+  head_sums<VPL>(q, s.head_log2, lane);
+  const auto yr = row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes);
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const float r = 1.0f / __builtin_sqrtf(q[j] * s.inv_h + s.eps);
+    store16<NT>(yr, L.off[j], E::scale(d[j], g, r));
+  }
+}
+
 // Weights for the team's slots when several rows share a workgroup: the
 // workgroup copies gamma into LDS once, by direct buffer-to-LDS loads (no
 // VGPRs involved), and every wavefront reads its slots from there. That is
@@ -381,7 +438,21 @@ template <class E, int V, int VPL, int NW, int MODE, bool MASKED, bool NT, bool 
 __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wave, int lane, float* part,
                                      u32x4* lds_g) {
   const Layout<V> L(tb, s, wave, lane);
-  if constexpr (PIPE) {
+  if constexpr (MODE == MODE_HEAD) {
+    int gi = blockIdx.x;
+    int64_t row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
+    u32x4 d[V];
+    load_row<E, V, NT>(d, row_rsrc<E>(s.x, s.x_stride, row, row < s.T, s.row_bytes), L);
+    const u32x4 g = load16<false>(rsrc(s.gamma, 16u << s.head_log2),
+                                  static_cast<uint32_t>(lane & ((1 << s.head_log2) - 1)) * 16u);
+    head_finish<E, V, NT>(d, g, s, L, row, row < s.T, lane);
+    for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
+      row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
+      u32x4 d2[V];
+      load_row<E, V, NT>(d2, row_rsrc<E>(s.x, s.x_stride, row, row < s.T, s.row_bytes), L);
+      head_finish<E, V, NT>(d2, g, s, L, row, row < s.T, lane);
+    }
+  } else if constexpr (PIPE) {
     fwd_pipelined<E, V, MASKED, NT>(s, L, wave, lane, part);
   } else {
     // The first group needs no bounds check (a group past the end holds only
@@ -465,6 +536,8 @@ hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hi
       hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, false>), gd, bd, lds, st, a);
     else
       hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false, false>), gd, bd, lds, st, a);
+  } else if (v.mode == MODE_HEAD) {
+    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_HEAD, false, true, false>), gd, bd, lds, st, a);
   } else if (v.mode == MODE_STATS) {
     hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, false, true, false>), gd, bd, lds, st, a);
   } else {

@@ -15,6 +15,11 @@
 // When that would need too many slots (many slices narrower than the team),
 // the kernel falls back to the "masked" layout: plain strided vectors, and a
 // per-lane slice index selects which partial each vector's squares join.
+//
+// Headwise rows use the one-slice (strided) layout. A head is a power of two
+// of at most 64 vectors, so each head sits in one slot of one aligned group
+// of lanes of one wavefront, and lane l always holds the head's vector
+// l mod (vectors per head): its weights are the same in every slot.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,6 +31,7 @@ enum Mode : int {
   MODE_FWD = 0,    // statistic and scaling in one pass (row stays in registers)
   MODE_STATS = 1,  // statistic only: one fp32 per row to `stats_out`
   MODE_APPLY = 2,  // combine `comb_k` precomputed partials, then scale
+  MODE_HEAD = 3,   // headwise: every head of 2^head_log2 vectors has its own statistic
 };
 
 constexpr int kMaxSlots = 16;  // slots per lane of the widest compiled variant
@@ -36,8 +42,8 @@ constexpr int kMaxSlots = 16;  // slots per lane of the widest compiled variant
 // u * slice_vec to the base and owns slices u, u + nsub, u + 2 nsub, ...
 struct Seg {
   const void* x;          // row 0 of the input
-  void* y;                // row 0 of the output (FWD, APPLY)
-  const void* gamma;      // weights of the columns processed (FWD, APPLY)
+  void* y;                // row 0 of the output (FWD, APPLY, HEAD)
+  const void* gamma;      // weights of the columns processed (FWD, APPLY); HEAD: of one head
   const float* stats_in;  // APPLY: partials laid out [comb_k][T]
   float* stats_out;       // STATS: row t's sum goes to stats_out[t]
   int64_t x_stride;       // elements between input rows
@@ -55,6 +61,8 @@ struct Seg {
   float inv_slice_vec;    // masked layout: 1.0f / slice_vec
   float h;                // the mean of squares divides by this width
   uint32_t flush_mask;    // segmented layout: bit j set when slot j ends a slice
+  int32_t head_log2;      // HEAD: log2 of the 16-byte vectors per head (0 ... 6)
+  float inv_h;            // HEAD: 1 / head width (a power of two, so exact)
   int32_t slot_base[kMaxSlots];
   int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
 };

@@ -12,7 +12,8 @@ weights nor the dataset are available, so seeded draws of the same shapes
 and value spreads are used instead.
 
 Recipe: numpy `default_rng([workload_id, tensor_id])` with tensor ids
-q=0, k=1, gamma_q=2, gamma_k=3, outlier mask for q=4, for k=5. Values are
+q=0, k=1, gamma_q=2, gamma_k=3, outlier mask for q=4, for k=5, and the
+per-head weights of the headwise form q=6, k=7. Values are
 drawn in float32; bf16 tensors are then rounded to nearest-even by torch.
 The bf16 values are the problem instance.
 """
@@ -24,7 +25,11 @@ import torch
 
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
-TENSOR_Q, TENSOR_K, TENSOR_GQ, TENSOR_GK, MASK_Q, MASK_K = range(6)
+TENSOR_Q, TENSOR_K, TENSOR_GQ, TENSOR_GK, MASK_Q, MASK_K, TENSOR_HGQ, TENSOR_HGK = range(8)
+
+# Head width of each workload's model, for the headwise form (the OLMo2
+# shapes use 128-wide heads; the tiny fp32 case cuts its rows into 4 heads).
+HEAD_DIM = {"c1": 64, "c2": 128, "c3": 128, "c4": 128, "c5": 128}
 
 
 @dataclass(frozen=True)
@@ -110,6 +115,14 @@ def weights(w, which):
     """Seeded gamma of workload `w` for tensor "q" or "k"."""
     tid, width = (TENSOR_GQ, w.hq) if which == "q" else (TENSOR_GK, w.hk)
     g = np.random.default_rng([w.wid, tid]).uniform(w.gamma_lo, w.gamma_hi, width)
+    return _finish(g.astype(np.float32), w.dtype)
+
+
+def head_weights(w, which, head_dim):
+    """Seeded weights of one head (head_dim of them, shared by every head of
+    the tensor) for the headwise form; tensor ids 6 (q) and 7 (k)."""
+    tid = TENSOR_HGQ if which == "q" else TENSOR_HGK
+    g = np.random.default_rng([w.wid, tid]).uniform(w.gamma_lo, w.gamma_hi, head_dim)
     return _finish(g.astype(np.float32), w.dtype)
 
 

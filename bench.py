@@ -71,6 +71,9 @@ def parse():
     p.add_argument("--cached-rows", type=int, default=0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also launch a plain elementwise copy of known size (counter calibration)")
+    p.add_argument("--main-only", action="store_true",
+                   help="time only the main forward (no other slicing, copy, latency, headwise or "
+                        "split-path figures): the profiler runs use this")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -104,16 +107,21 @@ def cpu_baseline(d, num_slices, seconds):
     for _ in range(reps):
         oracle.qk_forward(qs[:rows], ks[:rows], gq, gk, w.eps, num_slices)
     total = time.perf_counter() - t0
-    # the same oracle on one thread, over a smaller sample (about a fifth of the time)
+    # the same oracle on one thread, for about a fifth of the time
     oracle.set_threads(1)
-    rows1 = max(1, min(rows, int(rows * reps * (seconds / 5.0) / (cores * seconds))))
     t0 = time.perf_counter()
-    oracle.qk_forward(qs[:rows1], ks[:rows1], gq, gk, w.eps, num_slices)
+    oracle.qk_forward(qs[:rows], ks[:rows], gq, gk, w.eps, num_slices)
+    one = time.perf_counter() - t0
+    reps1 = max(1, int(seconds / 5.0 / max(one, 1e-6)))
+    t0 = time.perf_counter()
+    for _ in range(reps1):
+        oracle.qk_forward(qs[:rows], ks[:rows], gq, gk, w.eps, num_slices)
     one = time.perf_counter() - t0
     return {"value": rows * reps / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "%d of %d tokens (q %d + k %d columns, %s), K=%d, %d passes in %.1f s" % (
                 rows, w.T, w.hq, w.hk, w.dtype, num_slices, reps, total),
-            "one_thread": {"value": rows1 / one, "unit": "tokens/s", "sample": "%d tokens, %.1f s" % (rows1, one)},
+            "one_thread": {"value": rows * reps1 / one, "unit": "tokens/s",
+                           "sample": "%d tokens, %d passes in %.1f s" % (rows, reps1, one)},
             "host_cpus": os.cpu_count()}
 
 
@@ -172,6 +180,65 @@ def split_path(torch, qk, w, sets, gq, gk, ctx, stream, timed, K, args):
         "whole_gbs": whole_bytes / (whole_ms * 1e-3) / 1e9,
         "rank_share_us": rank_ms * 1e3, "rank_share_launches": 4, "rank_share_bytes": rank_bytes,
         "rank_share_gbs": rank_bytes / (rank_ms * 1e-3) / 1e9}}
+
+
+def secondary(torch, qk, workloads, w, args, K, sets, gq, gk, ctx, stream, dev, timed, step):
+    """Figures next to the main one: the workload's other slice count, a
+    same-bytes device copy (the achievable-bandwidth ceiling), the host's
+    call-to-completion latency, the headwise form over the same rows, and the
+    split path."""
+    eb = w.elem_bytes
+    extra = {}
+    for k_alt in w.slices:
+        if k_alt == K:
+            continue
+        for i in range(args.warmup):
+            step(i, k_alt)
+        extra["kernel_us_K%d" % k_alt] = timed(args.steps, lambda i: step(i, k_alt))[0] * 1e3
+    nb = w.T * (w.hq + w.hk) * eb
+    csets = max(2, math.ceil(args.rotate_mib * 2**20 / (2 * nb)))
+    cbufs = [(torch.empty(nb, dtype=torch.uint8, device=dev), torch.empty(nb, dtype=torch.uint8, device=dev))
+             for _ in range(csets)]
+    for s_, t_ in cbufs:
+        t_.copy_(s_)
+    copy_ms = timed(args.steps, lambda i: cbufs[i % csets][1].copy_(cbufs[i % csets][0]))[0]
+    del cbufs
+    extra["copy_same_bytes_us"] = copy_ms * 1e3
+    extra["copy_same_bytes_gbs"] = 2 * nb / (copy_ms * 1e-3) / 1e9
+
+    # host view of one call: enqueue, then wait for completion (decode latency)
+    lat = []
+    for i in range(min(args.steps, 200)):
+        t0 = time.perf_counter()
+        step(i)
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - t0) * 1e6)
+    lat.sort()
+    extra["host_call_to_done_us_p10_p50_p90"] = [lat[len(lat) // 10], lat[len(lat) // 2],
+                                                  lat[(9 * len(lat)) // 10]]
+
+    # headwise QK-Norm over the same rows (heads of the model's width)
+    D = workloads.HEAD_DIM[args.workload]
+    hgq = workloads.head_weights(w, "q", D).to(dev)
+    hgk = workloads.head_weights(w, "k", D).to(dev)
+
+    def head_step(i):
+        q, k, yq, yk = sets[i % len(sets)]
+        qk.forward_headwise(q, k, hgq, hgk, D, eps=w.eps, out_q=yq, out_k=yk, ctx=ctx, stream=stream)
+
+    for i in range(args.warmup):
+        head_step(i)
+    head_ms = timed(args.steps, head_step)[0]
+    head_bytes = 2 * w.T * (w.hq + w.hk) * eb + 2 * D * eb
+    extra["headwise"] = {"head_dim": D, "kernel_us": head_ms * 1e3, "algorithmic_bytes": head_bytes,
+                         "gbs": head_bytes / (head_ms * 1e-3) / 1e9,
+                         "frac": head_bytes / (head_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+    # the split path (partial statistics, then apply) over the same rows
+    if max(w.slices) > 1:
+        extra.update(split_path(torch, qk, w, sets, gq, gk, ctx, stream, timed, max(w.slices), args))
+
+    return extra
 
 
 def main():
@@ -275,38 +342,9 @@ def main():
     per = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
     ev_p10, ev_p50, ev_p90 = per[len(per) // 10], per[len(per) // 2], per[(9 * len(per)) // 10]
 
-    # the other slicing of the same workload, and a same-bytes device copy
     extra = {}
-    for k_alt in w.slices:
-        if k_alt == K:
-            continue
-        for i in range(args.warmup):
-            step(i, k_alt)
-        extra["kernel_us_K%d" % k_alt] = timed(args.steps, lambda i: step(i, k_alt))[0] * 1e3
-    nb = w.T * (w.hq + w.hk) * eb
-    csets = max(2, math.ceil(args.rotate_mib * 2**20 / (2 * nb)))
-    cbufs = [(torch.empty(nb, dtype=torch.uint8, device=dev), torch.empty(nb, dtype=torch.uint8, device=dev))
-             for _ in range(csets)]
-    for s_, t_ in cbufs:
-        t_.copy_(s_)
-    copy_ms = timed(args.steps, lambda i: cbufs[i % csets][1].copy_(cbufs[i % csets][0]))[0]
-    del cbufs
-
-    # host view of one call: enqueue, then wait for completion (decode latency)
-    lat = []
-    for i in range(min(args.steps, 200)):
-        t0 = time.perf_counter()
-        step(i)
-        torch.cuda.synchronize()
-        lat.append((time.perf_counter() - t0) * 1e6)
-    lat.sort()
-    extra["host_call_to_done_us_p10_p50_p90"] = [lat[len(lat) // 10], lat[len(lat) // 2],
-                                                  lat[(9 * len(lat)) // 10]]
-
-    # the split path (partial statistics, then apply) over the same rows
-    if max(w.slices) > 1:
-        extra.update(split_path(torch, qk, w, sets, gq, gk, ctx, stream, timed, max(w.slices), args))
-
+    if not args.main_only:
+        extra.update(secondary(torch, qk, workloads, w, args, K, sets, gq, gk, ctx, stream, dev, timed, step))
     achieved_gbs = algo_bytes / (kern_ms * 1e-3) / 1e9
     traffic = None
     tf = os.path.join(ROOT, TRAFFIC_FILE.format(workload=args.workload))
@@ -340,8 +378,6 @@ def main():
         "kernel_us": kern_ms * 1e3,
         "host_enqueue_us_per_launch": host_us / args.steps,
         "event_pair_us_p10_p50_p90": [ev_p10 * 1e3, ev_p50 * 1e3, ev_p90 * 1e3],
-        "copy_same_bytes_us": copy_ms * 1e3,
-        "copy_same_bytes_gbs": 2 * nb / (copy_ms * 1e-3) / 1e9,
         "kernel_source_sha": kernel_source_sha(),
     }
     result.update({k2: v for k2, v in extra.items()})

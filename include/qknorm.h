@@ -63,7 +63,8 @@ typedef enum {
                                 h_total < width                                   */
     QKNORM_ERR_SLICES = -3,  /* num_slices outside [1, 64], width not cut evenly,
                                 slice width not whole vectors, slice_index out of
-                                range                                             */
+                                range; or head_dim not a valid head width, or
+                                width not a whole number of heads               */
     QKNORM_ERR_ALIGN = -4,   /* pointer not 16-byte aligned, or width / stride not
                                 a whole number of 16-byte vectors                 */
     QKNORM_ERR_DTYPE = -5,   /* dtype is not a qknorm_dtype                         */
@@ -138,6 +139,33 @@ int qknorm_forward(qknorm_ctx *ctx, int dtype, int64_t T,
                    const qknorm_rows *q, const qknorm_rows *k,
                    const void *gamma_q, const void *gamma_k,
                    float eps, int num_slices, void *stream);
+
+/*
+ * Fused headwise QK-Norm over the query rows and the key rows of T tokens
+ * (SwiftQK review, "Layerwise vs. headwise QK-Norm": one normalisation
+ * factor per attention head, the case the layerwise form is contrasted
+ * with). Each row holds width / head_dim heads of head_dim contiguous
+ * columns, head 0 first; every head is normalised by Eq. 1 over its own
+ * columns only (its own sum of squares, the mean over head_dim, eps inside
+ * the square root), and the head_dim weights of a tensor are shared by all
+ * of its heads. One kernel launch; each row is read once and written once.
+ *
+ *   head_dim   columns per head, the same for q and k: one head must be a
+ *              power of two of 16-byte vectors, at most 64 of them (bf16:
+ *              8, 16, ..., 512 columns; fp32: 4, 8, ..., 256), and each
+ *              width a multiple of head_dim
+ *   gamma_q, gamma_k  head_dim weights each (element type of the rows)
+ *   dtype, T, q, k, eps, stream: as for qknorm_forward
+ * Rows are always streamed (the cached_rows option does not apply).
+ * Status, in validation order: QKNORM_ERR_DTYPE, QKNORM_ERR_SHAPE (T < 0),
+ * then for q and k in turn QKNORM_ERR_NULL, QKNORM_ERR_SHAPE,
+ * QKNORM_ERR_ALIGN, QKNORM_ERR_SLICES (head_dim), then QKNORM_ERR_EPS,
+ * QKNORM_ERR_ALIAS, QKNORM_ERR_CONTEXT, QKNORM_ERR_DEVICE.
+ */
+int qknorm_forward_headwise(qknorm_ctx *ctx, int dtype, int64_t T,
+                            const qknorm_rows *q, const qknorm_rows *k,
+                            const void *gamma_q, const void *gamma_k,
+                            int64_t head_dim, float eps, void *stream);
 
 /*
  * Split path, step 1: one slice's partial sums of squares (Algorithm 1,

@@ -9,7 +9,10 @@
 //    its flush bit set, and the i-th flush is slice sub + i * nsub, which is
 //    where the LDS combine looks for it;
 //  - the slot count fits a compiled variant, and staged gamma fits the
-//    copy loop's bound.
+//    copy loop's bound;
+//  - headwise plans keep every head inside one aligned lane group of one
+//    wavefront and slot, lane l holding the head's vector l mod (vectors
+//    per head).
 #include "qknorm_api.cpp"
 
 #include <cstdio>
@@ -136,6 +139,59 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
   for (int i = 0; i < nseg; ++i) check_seg(seg[i], nw, vpl, in[i].nvec, K, masked, what);
 }
 
+// Headwise: each aligned group of hv lanes of one wavefront holds, in each
+// slot, either nothing or the hv vectors of one head in order, so lane l
+// holds the head's vector l mod hv (the kernel's head sum and weights).
+static void check_heads(const qkn::Seg& s, int hv, const char* what) {
+  const int wl = s.wpr_log2, m = s.sub_log2, lanes = 64 << wl;
+  for (int j = 0; j < s.nslot; ++j)
+    for (int g0 = 0; g0 < lanes; g0 += hv) {
+      const int v0 = qkn::slot_vector(s.slot_lim[j], s.slot_base[j], g0, wl, m, s.slice_vec, 1);
+      for (int i = 0; i < hv; ++i) {
+        const int v = qkn::slot_vector(s.slot_lim[j], s.slot_base[j], g0 + i, wl, m, s.slice_vec, 1);
+        if (v0 < 0) {
+          CHECK(v < 0, "%s slot %d group %d: lane %d live in an empty group", what, j, g0, i);
+          continue;
+        }
+        CHECK(v == v0 + i && v0 % hv == 0, "%s slot %d group %d: lane %d holds %d (group starts at %d)", what,
+              j, g0, i, v, v0);
+        CHECK(v < 0 || v % hv == ((g0 + i) & 63) % hv, "%s weights of lane %d", what, g0 + i);
+      }
+    }
+}
+
+static void run_headwise(int64_t T, int64_t hq, int64_t hk, int64_t D, int forced_wpr, int dtype) {
+  qknorm_ctx ctx{0, 256, qknorm_options{forced_wpr, 0, 0}};
+  const int64_t ve = vec_elems(dtype);
+  const int hv = head_vectors(D, dtype);
+  SegIn in[2] = {{hq / ve, 1}, {hk / ve, 1}};
+  const int nseg = hk > 0 ? 2 : 1;
+  Plan plans[2];
+  int nw = 4;
+  char what[160];
+  std::snprintf(what, sizeof what, "headwise T=%lld hq=%lld hk=%lld D=%lld wpr=%d dt=%d", (long long)T,
+                (long long)hq, (long long)hk, (long long)D, forced_wpr, dtype);
+  CHECK(hv > 0, "%s invalid head", what);
+  if (plan_launch(&ctx, in, nseg, T, plans, &nw) != QKNORM_OK) {
+    CHECK(forced_wpr != 0, "%s auto plan refused", what);
+    return;
+  }
+  qkn::Seg seg[2];
+  int slots = 0;
+  for (int i = 0; i < nseg; ++i) {
+    CHECK(!plans[i].masked, "%s masked plan", what);
+    fill_layout(&seg[i], plans[i], nw, in[i].nvec, 1, T);
+    slots = seg[i].nslot > slots ? seg[i].nslot : slots;
+  }
+  const int vpl = qkn::compiled_vpl(slots, nw);
+  CHECK(vpl > 0, "%s no compiled variant for %d slots", what, slots);
+  if (vpl == 0) return;
+  for (int i = 0; i < nseg; ++i) {
+    check_seg(seg[i], nw, vpl, in[i].nvec, 1, false, what);
+    check_heads(seg[i], hv, what);
+  }
+}
+
 int main() {
   int cases = 0;
   const int64_t widths[] = {8, 24, 64, 96, 200, 256, 512, 1000, 1024, 1032, 1280, 1536, 2048,
@@ -158,6 +214,17 @@ int main() {
               run_forward(T, hq, hk, K, w, dtype);
               ++cases;
             }
+          }
+      }
+  for (int dtype : {QKNORM_BF16, QKNORM_F32})
+    for (int64_t hq : widths)
+      for (int64_t D = 1; D <= hq; D *= 2) {
+        if (hq > qknorm_max_width(dtype) || head_vectors(D, dtype) == 0 || hq % D) continue;
+        for (int64_t T : rows)
+          for (int w : wprs) {
+            run_headwise(T, hq, 0, D, w, dtype);
+            run_headwise(T, hq, (hq / 4) % D == 0 && hq >= 4 * D ? hq / 4 : D, D, w, dtype);
+            cases += 2;
           }
       }
   std::printf("%d cases, %d failures\n", cases, failures);

@@ -153,6 +153,47 @@ def test_forward_in_place_and_packed_qkv_are_accepted(L):
     assert _fwd(L, q=q, k=k_bad) == qk.ERR_ALIAS
 
 
+def _head(L, dtype=qk.BF16, T=64, q=None, k="default", gq=A + 60 * MB, gk=A + 61 * MB, D=128, eps=1e-6):
+    if q is None:
+        q = qk.Rows(A, A + 8 * MB, 4096, 4096, 4096)
+    if k == "default":
+        k = qk.Rows(A + 16 * MB, A + 24 * MB, 1024, 1024, 1024)
+    return L.qknorm_forward_headwise(None, dtype, T, ctypes.byref(q),
+                                     ctypes.byref(k) if k is not None else None, gq, gk, D, eps, None)
+
+
+def test_headwise_validation(L):
+    R = qk.Rows
+    assert _head(L) == qk.ERR_CONTEXT
+    assert _head(L, k=None) == qk.ERR_CONTEXT
+    assert _head(L, T=0) == qk.OK
+    # valid head widths: a power of two of 16-byte vectors, at most 64 of them
+    for dtype, D in ((qk.BF16, 8), (qk.BF16, 64), (qk.BF16, 256), (qk.BF16, 512),
+                     (qk.F32, 4), (qk.F32, 128), (qk.F32, 256)):
+        assert _head(L, dtype=dtype, D=D) == qk.ERR_CONTEXT, (dtype, D)
+    for dtype, D in ((qk.BF16, 0), (qk.BF16, -128), (qk.BF16, 4), (qk.BF16, 96), (qk.BF16, 1024),
+                     (qk.BF16, 2048), (qk.F32, 2), (qk.F32, 512), (qk.F32, 192)):
+        assert _head(L, dtype=dtype, D=D) == qk.ERR_SLICES, (dtype, D)
+    # every width must be whole heads: 1024 / 512 is, 1152 / 256 is not
+    assert _head(L, D=512) == qk.ERR_CONTEXT
+    assert _head(L, D=256, k=R(A + 16 * MB, A + 24 * MB, 1152, 1152, 1152)) == qk.ERR_SLICES
+    cases = [
+        (dict(dtype=2), qk.ERR_DTYPE),
+        (dict(T=-1), qk.ERR_SHAPE),
+        (dict(gq=None), qk.ERR_NULL),
+        (dict(q=R(A, A + 8 * MB, 4096, 4088, 4096)), qk.ERR_SHAPE),
+        (dict(q=R(A + 2, A + 8 * MB, 4096, 4096, 4096)), qk.ERR_ALIGN),
+        (dict(eps=-1.0), qk.ERR_EPS),
+        (dict(q=R(A, A + 16, 4096, 4096, 4096)), qk.ERR_ALIAS),
+        # gamma holds head_dim weights: an output starting just past 128 bf16
+        # weights does not overlap them, one starting inside does
+        (dict(gq=A + 8 * MB - 256), qk.ERR_CONTEXT),
+        (dict(gq=A + 8 * MB - 240), qk.ERR_ALIAS),
+    ]
+    for kw, want in cases:
+        assert _head(L, **kw) == want, kw
+
+
 def _stats(L, dtype=qk.BF16, T=256, x=A, stride=5120, w=1280, s=0, K=4, st=A + 64 * MB):
     return L.qknorm_partial_stats(None, dtype, T, x, stride, w, s, K, st, None)
 

@@ -310,3 +310,141 @@ def test_empty_and_single_tensor():
     yq, yk = qk.forward(z, z, g, g)
     torch.cuda.synchronize()
     assert yq.shape == (0, 4096)
+
+
+# ---- headwise QK-Norm (one statistic per head) ---------------------------------
+
+def run_headwise(q, k, gq, gk, D, eps, in_place=False, ctx=None):
+    qd, kd = gpu(q), (gpu(k) if k is not None else None)
+    out_q = qd if in_place else None
+    out_k = kd if (in_place and kd is not None) else None
+    yq, yk = qk.forward_headwise(qd, kd, gpu(gq), gpu(gk) if gk is not None else None, D, eps=eps,
+                                 out_q=out_q, out_k=out_k, ctx=ctx)
+    torch.cuda.synchronize()
+    return yq, yk
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_headwise_workload_parity(name):
+    """The five workloads' rows cut into their models' heads, each head
+    normalised on its own (review, "Layerwise vs. headwise QK-Norm")."""
+    d = workloads.generate(name)
+    w = d["w"]
+    D = workloads.HEAD_DIM[name]
+    gq, gk = workloads.head_weights(w, "q", D), workloads.head_weights(w, "k", D)
+    say("headwise", name, "T=%d Hq=%d Hk=%d %s head_dim=%d in_place=%s" % (w.T, w.hq, w.hk, w.dtype, D,
+                                                                           w.in_place))
+    yq, yk = run_headwise(d["q"], d["k"], gq, gk, D, w.eps, in_place=w.in_place)
+    rq, rk = oracle.qk_headwise(d["q"], d["k"], gq, gk, D, w.eps)
+    print("  q errors", assert_parity(yq, rq, w.torch_dtype, name + " headwise q"), flush=True)
+    print("  k errors", assert_parity(yk, rk, w.torch_dtype, name + " headwise k"), flush=True)
+
+
+HEAD_CASES = [
+    # dtype, T, Hq, Hk, head_dim: every head width from one vector to 64,
+    # ragged slots, teams of several wavefronts, rows past the grid
+    ("bf16", 37, 2048, 512, 8),
+    ("bf16", 37, 2048, 512, 16),
+    ("bf16", 37, 2048, 512, 32),
+    ("bf16", 37, 2048, 512, 64),
+    ("bf16", 37, 5120, 1024, 128),
+    ("bf16", 5, 5120, 1536, 256),
+    ("bf16", 9, 8192, 512, 512),
+    ("bf16", 3, 65536, 512, 512),     # widest bf16 row: 16-wavefront teams
+    ("bf16", 2000, 1024, 128, 128),   # many rows per SIMD
+    ("f32", 21, 1024, 256, 4),
+    ("f32", 21, 1024, 256, 32),
+    ("f32", 21, 3072, 256, 64),
+    ("f32", 11, 4096, 512, 128),
+    ("f32", 11, 4096, 1280, 256),
+    ("f32", 1, 256, 256, 256),        # one head: the layerwise norm
+]
+
+
+@pytest.mark.parametrize("dtype,T,Hq,Hk,D", HEAD_CASES)
+def test_headwise_shapes(dtype, T, Hq, Hk, D):
+    q = workloads.random_rows(T, Hq, dtype, [T, Hq, D, 1], dist="laplace")
+    k = workloads.random_rows(T, Hk, dtype, [T, Hk, D, 2], scale=3.0)
+    # give the heads very different scales, so a statistic taken over the
+    # wrong columns shows
+    q = (q.float() * torch.linspace(0.01, 10.0, Hq // D).repeat_interleave(D)).to(q.dtype)
+    gq = workloads.random_weights(D, dtype, [D, 3])
+    gk = workloads.random_weights(D, dtype, [D, 4])
+    say("headwise", dtype, T, Hq, Hk, D)
+    yq, yk = run_headwise(q, k, gq, gk, D, 1e-6)
+    rq, rk = oracle.qk_headwise(q, k, gq, gk, D, 1e-6)
+    assert_parity(yq, rq, workloads.DTYPES[dtype], "q")
+    assert_parity(yk, rk, workloads.DTYPES[dtype], "k")
+
+
+def test_headwise_closed_form_on_gpu():
+    """The worked example's row in two heads of 4: with eps = 0 the first
+    head's RMS is exactly 1.25, the second head's sqrt(3.875)."""
+    x = torch.tensor([[1.0, 2.0, -1.0, 0.5, 3.0, -2.0, 1.5, 0.5]])
+    r1 = 1.0 / np.sqrt(3.875)
+    say("headwise closed form")
+    y, _ = run_headwise(x, None, torch.ones(4), None, 4, 0.0)
+    ref = np.array([[0.8, 1.6, -0.8, 0.4, 3.0 * r1, -2.0 * r1, 1.5 * r1, 0.5 * r1]])
+    assert_parity(y, ref, torch.float32, "heads of 4")
+    y, _ = run_headwise(x, None, torch.tensor([1.0, 0.5, 2.0, 4.0]), None, 4, 0.0)
+    ref = np.array([[0.8, 0.8, -1.6, 1.6, 3.0 * r1, -1.0 * r1, 3.0 * r1, 2.0 * r1]])
+    assert_parity(y, ref, torch.float32, "shared weights")
+
+
+@pytest.mark.parametrize("opts", [dict(waves_per_row=1), dict(waves_per_row=2), dict(waves_per_row=4),
+                                  dict(waves_per_row=16), dict(max_workgroups=7),
+                                  dict(max_workgroups=2, waves_per_row=4)],
+                         ids=lambda o: ",".join("%s=%s" % kv for kv in o.items()))
+def test_headwise_schedules_agree(opts):
+    ctx = qk.Context(0, **opts)
+    for dtype, T, Hq, Hk, D in (("bf16", 131, 5120, 1024, 128), ("f32", 45, 2048, 512, 64),
+                                ("bf16", 19, 1024, 64, 64)):
+        q = workloads.random_rows(T, Hq, dtype, [17, T])
+        k = workloads.random_rows(T, Hk, dtype, [18, T])
+        gq = workloads.random_weights(D, dtype, 19)
+        gk = workloads.random_weights(D, dtype, 20)
+        say("headwise schedule", opts, dtype, T, Hq, Hk, D)
+        try:
+            yq, yk = run_headwise(q, k, gq, gk, D, 1e-6, ctx=ctx)
+        except qk.QKNormError as e:
+            assert e.status == qk.ERR_SHAPE and "waves_per_row" in opts
+            continue
+        rq, rk = oracle.qk_headwise(q, k, gq, gk, D, 1e-6)
+        assert_parity(yq, rq, workloads.DTYPES[dtype], "q")
+        assert_parity(yk, rk, workloads.DTYPES[dtype], "k")
+
+
+def test_headwise_packed_qkv_in_place():
+    """Headwise norm of the query and key columns of a packed QKV buffer, in
+    place; the value columns stay untouched."""
+    T, Hq, Hk, Hv, D = 33, 2048, 256, 256, 128
+    H = Hq + Hk + Hv
+    qkv = workloads.random_rows(T, H, "bf16", 85)
+    gq = workloads.random_weights(D, "bf16", 86)
+    gk = workloads.random_weights(D, "bf16", 87)
+    rq, rk = oracle.qk_headwise(qkv[:, :Hq], qkv[:, Hq:Hq + Hk], gq, gk, D, 1e-6)
+    dev = gpu(qkv)
+    q, k = dev[:, :Hq], dev[:, Hq:Hq + Hk]
+    say("headwise packed qkv in place")
+    qk.forward_headwise(q, k, gpu(gq), gpu(gk), D, eps=1e-6, out_q=q, out_k=k)
+    torch.cuda.synchronize()
+    out = dev.cpu()
+    assert_parity(out[:, :Hq], rq, torch.bfloat16, "q")
+    assert_parity(out[:, Hq:Hq + Hk], rk, torch.bfloat16, "k")
+    assert torch.equal(out[:, Hq + Hk:], qkv[:, Hq + Hk:])
+
+
+def test_headwise_zero_heads_and_reproducibility():
+    """A head of zeros gives zeros (eps > 0) while its neighbours are
+    normalised normally; repeated calls are bitwise identical."""
+    T, H, D = 6, 1024, 128
+    x = workloads.random_rows(T, H, "bf16", 88)
+    x[:, 2 * D:3 * D] = 0.0
+    g = workloads.random_weights(D, "bf16", 89)
+    say("headwise zero head")
+    y1, _ = run_headwise(x, None, g, None, D, 1e-6)
+    y2, _ = run_headwise(x, None, g, None, D, 1e-6)
+    assert torch.equal(y1, y2)
+    assert (y1[:, 2 * D:3 * D] == 0).all()
+    ref, _ = oracle.qk_headwise(x, x, g, g, D, 1e-6)
+    assert_parity(y1, ref, torch.bfloat16, "zero head")
