@@ -41,14 +41,17 @@ def load(path):
     L.oracle_forward.restype = None
     L.oracle_headwise.argtypes = [_fp, i64, i64, i64, i64, _fp, ctypes.c_double, _dp, i64]
     L.oracle_headwise.restype = None
+    L.oracle_inv_rms.argtypes = [_fp, i64, i64, i64, ctypes.c_int, ctypes.c_double, _dp, _dp]
+    L.oracle_inv_rms.restype = None
     return L
 
 
 def lib():
-    """Load (building first if the shared object is missing) the C oracle."""
+    """Load the C oracle, building it first when the shared object is missing
+    or older than its source."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        if not os.path.exists(_build.LIB) or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC):
             _build.build()
         _lib = load(_build.LIB)
     return _lib
@@ -197,3 +200,18 @@ def qk_headwise(q, k, gamma_q, gamma_k, head_dim, eps):
     """Headwise QK-Norm of the query rows and the key rows, each tensor with
     its own head_dim-long weights. Returns (y_q, y_k) in float64."""
     return headwise(q, gamma_q, head_dim, eps), headwise(k, gamma_k, head_dim, eps)
+
+
+def inv_rms(x, eps, num_slices=1):
+    """Per-token inverse RMS 1 / sqrt(S / H + eps) (review Eq. 6), with S the
+    ascending sum of `num_slices` slice sums. x: [T, H]. Returns float64 [T]."""
+    x = _rows(x)
+    T, H = x.shape
+    K = int(num_slices)
+    if K < 1 or H % K:
+        raise ValueError("width %d is not cut evenly into %d slices" % (H, K))
+    P = np.empty((K, T), dtype=np.float64)
+    r = np.empty(T, dtype=np.float64)
+    lib().oracle_inv_rms(x.ctypes.data_as(_fp), T, H, H, K, eps_as_gpu_sees_it(eps),
+                         P.ctypes.data_as(_dp), r.ctypes.data_as(_dp))
+    return r

@@ -144,3 +144,25 @@ void oracle_headwise(const float *x, int64_t T, int64_t H, int64_t ldx,
         }
     }
 }
+
+/*
+ * The per-token inverse RMS alone (review Eq. 6; the statistic a consumer
+ * applies itself when the scaling is deferred to it). The sum of squares is
+ * formed as in oracle_forward: K slice sums in ascending column order, added
+ * in ascending slice order (Eq. 5); the mean divides by the full width H.
+ *   r : out, r[t] = 1 / sqrt( S_t / H + eps )
+ * P is caller scratch of K*T doubles and holds the partials on return.
+ */
+void oracle_inv_rms(const float *x, int64_t T, int64_t H, int64_t ldx,
+                    int K, double eps, double *P, double *r)
+{
+    oracle_slice_sumsq(x, T, H, ldx, K, P);
+    int64_t t;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (t = 0; t < T; ++t) {
+        double S = 0.0;
+        for (int s = 0; s < K; ++s)
+            S += P[(int64_t)s * T + t];
+        r[t] = 1.0 / sqrt(S / (double)H + eps);
+    }
+}

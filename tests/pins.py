@@ -296,6 +296,30 @@ def pin_headwise_reductions():
     np.testing.assert_allclose((y0 * y0).mean(axis=2), 1.0, rtol=1e-13)
 
 
+def pin_inv_rms():
+    """The inverse RMS on its own: Eq. 6's printed 0.6065 (and the exact
+    value from rational arithmetic) for the worked example with K = 2 and 1,
+    exactly 0.8 for the four-element shard with eps = 0, and, on general
+    rows, the factor that turns x * gamma into the forward's output."""
+    g = read_golden("swiftqk_worked_example.txt")
+    x = _ex(g["x"])
+    eps = oracle.eps_as_gpu_sees_it(g["eps"][0])
+    exact_r = float(1 / exact._dec(exact.sum_of_squares(x[0]) / 8 + exact.Fraction(eps)).sqrt())
+    for K in (2, 1):
+        r = oracle.inv_rms(x, g["eps"][0], K)
+        assert abs(r[0] - g["rms_inv"][0]) <= 0.5 * 10 ** -g["rms_inv_digits"][0], ("Eq. 6", K, r[0])
+        assert abs(r[0] - exact_r) <= 1e-16, (K, r[0], exact_r)
+    assert oracle.inv_rms(_ex([1.0, 2.0, -1.0, 0.5]), 0.0, 1)[0] == 0.8
+    assert oracle.inv_rms(_ex([1.0, 2.0, -1.0, 0.5]), 0.0, 2)[0] == 0.8
+    xs = workloads.random_rows(9, 640, "f32", 91).numpy()
+    gs = workloads.random_weights(640, "f32", 92).numpy()
+    y, _ = oracle.forward(xs, gs, 1e-6, 5)
+    r = oracle.inv_rms(xs, 1e-6, 5)
+    np.testing.assert_allclose(y, xs.astype(np.float64) * r[:, None] * gs.astype(np.float64), rtol=1e-15)
+    # a constant row a: 1 / sqrt(a^2 + eps)
+    assert abs(oracle.inv_rms(np.full((1, 64), 0.75, F32), 1e-6, 4)[0] - 1 / math.sqrt(0.5625 + eps)) < 1e-15
+
+
 ALL_PINS = [
     pin_worked_example_printed,
     pin_worked_example_exact,
@@ -310,4 +334,5 @@ ALL_PINS = [
     pin_headwise_closed_form,
     pin_headwise_exact_rows,
     pin_headwise_reductions,
+    pin_inv_rms,
 ]

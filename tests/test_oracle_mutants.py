@@ -21,6 +21,10 @@ MUTANTS = [
     ("output_sign", "out[j] = (double)row[j]", "out[j] = -(double)row[j]"),
     ("abs_not_square", "acc += v * v;", "acc += v < 0 ? -v : v;"),
     ("first_slice_only", "for (int s = 0; s < K; ++s) /* Eq. 5", "for (int s = 0; s < 1; ++s) /* Eq. 5"),
+    # inverse RMS alone
+    ("rinv_over_slice", "r[t] = 1.0 / sqrt(S / (double)H + eps);", "r[t] = 1.0 / sqrt(S / (double)(H / K) + eps);"),
+    ("rinv_rms_not_inverse", "r[t] = 1.0 / sqrt(S / (double)H + eps);", "r[t] = sqrt(S / (double)H + eps);"),
+    ("rinv_first_slice", "for (int s = 0; s < K; ++s)\n            S += P", "for (int s = 0; s < 1; ++s)\n            S += P"),
     # headwise
     ("head_mean_over_row", "sqrt(S / (double)D + eps)", "sqrt(S / (double)H + eps)"),
     ("head_eps_outside_sqrt", "sqrt(S / (double)D + eps)", "(sqrt(S / (double)D) + eps)"),
