@@ -27,8 +27,8 @@ ERR_NULL, ERR_SHAPE, ERR_SLICES, ERR_ALIGN, ERR_DTYPE, ERR_EPS, ERR_ALIAS, ERR_D
 
 # Every symbol include/qknorm.h declares.
 EXPORTS = ("qknorm_create", "qknorm_create_ex", "qknorm_destroy", "qknorm_forward",
-           "qknorm_forward_headwise", "qknorm_partial_stats", "qknorm_apply_stats",
-           "qknorm_status_string", "qknorm_max_width")
+           "qknorm_forward_headwise", "qknorm_inv_rms", "qknorm_partial_stats",
+           "qknorm_apply_stats", "qknorm_status_string", "qknorm_max_width")
 
 
 class Rows(ctypes.Structure):
@@ -71,6 +71,8 @@ def lib():
                                          vp, vp, cf, ci, vp]
             L.qknorm_forward_headwise.argtypes = [vp, ci, i64, ctypes.POINTER(Rows), ctypes.POINTER(Rows),
                                                   vp, vp, i64, cf, vp]
+            L.qknorm_inv_rms.argtypes = [vp, ci, i64, ctypes.POINTER(Rows), ctypes.POINTER(Rows), cf, ci,
+                                         vp, vp, vp]
             L.qknorm_partial_stats.argtypes = [vp, ci, i64, vp, i64, i64, ci, ci, vp, vp]
             L.qknorm_apply_stats.argtypes = [vp, ci, i64, ctypes.POINTER(Rows), vp, vp, ci, i64,
                                              cf, vp]
@@ -79,7 +81,8 @@ def lib():
             L.qknorm_max_width.argtypes = [ci]
             L.qknorm_max_width.restype = i64
             for name in ("qknorm_create", "qknorm_create_ex", "qknorm_destroy", "qknorm_forward",
-                         "qknorm_forward_headwise", "qknorm_partial_stats", "qknorm_apply_stats"):
+                         "qknorm_forward_headwise", "qknorm_inv_rms", "qknorm_partial_stats",
+                         "qknorm_apply_stats"):
                 getattr(L, name).restype = ci
             _lib = L
         return _lib
@@ -227,6 +230,38 @@ def forward_headwise(q, k, gamma_q, gamma_k, head_dim, eps=1e-6, out_q=None, out
                                        int(head_dim), float(eps), _stream_of(q, stream))
     _check(st, "qknorm_forward_headwise")
     return out_q, out_k
+
+
+def inv_rms(q, k=None, eps=1e-6, num_slices=1, out_q=None, out_k=None, ctx=None, stream=None):
+    """Per-token inverse RMS 1 / sqrt(S / width + eps) of the rows of q
+    [T, Hq] and k [T, Hk] (k may be None), in one launch: the factor
+    forward() scales each row by, for a consumer that applies it itself.
+    Returns (r_q, r_k), float32 [T] each (new tensors unless out_* given)."""
+    torch = _torch()
+    dt = _dtype_code(q)
+    T = q.shape[0]
+    rq = _rows_of(q, None)
+    rk = None
+    if k is not None:
+        if k.shape[0] != T or k.dtype != q.dtype:
+            raise ValueError("q and k must share T and dtype")
+        rk = _rows_of(k, None)
+    outs = []
+    for o, x in ((out_q, q), (out_k, k)):
+        if x is None:
+            outs.append(None)
+            continue
+        if o is None:
+            o = torch.empty(T, dtype=torch.float32, device=x.device)
+        if o.dtype != torch.float32 or o.shape != (T,) or not o.is_contiguous():
+            raise ValueError("inverse-RMS outputs are contiguous float32 [T] tensors")
+        outs.append(o)
+    c = _ctx_of(q, ctx)
+    st = lib().qknorm_inv_rms(c.handle, dt, T, ctypes.byref(rq), ctypes.byref(rk) if rk is not None else None,
+                              float(eps), int(num_slices), outs[0].data_ptr(),
+                              outs[1].data_ptr() if outs[1] is not None else None, _stream_of(q, stream))
+    _check(st, "qknorm_inv_rms")
+    return outs[0], outs[1]
 
 
 def partial_stats(x_slice, slice_index, num_slices, stats=None, ctx=None, stream=None):

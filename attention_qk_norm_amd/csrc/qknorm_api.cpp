@@ -514,6 +514,65 @@ int qknorm_forward_headwise(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_
   return run(ctx, v, a, nseg, stream);
 }
 
+int qknorm_inv_rms(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, const qknorm_rows* k, float eps,
+                   int num_slices, float* rinv_q, float* rinv_k, void* stream) {
+  if (!valid_dtype(dtype)) return QKNORM_ERR_DTYPE;
+  if (T < 0 || T > kMaxRows) return QKNORM_ERR_SHAPE;
+  if (T == 0) return QKNORM_OK;
+  const qknorm_rows* segs[2] = {q, k};
+  float* outs[2] = {rinv_q, rinv_k};
+  const int nseg = k != nullptr ? 2 : 1;
+  const int64_t ve = vec_elems(dtype);
+  for (int i = 0; i < nseg; ++i) {
+    if (outs[i] == nullptr) return QKNORM_ERR_NULL;
+    const int st = check_rows(segs[i], nullptr, dtype, false, false);
+    if (st != QKNORM_OK) return st;
+    if (segs[i]->width > qknorm_max_width(dtype)) return QKNORM_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(outs[i]) & 3u) != 0) return QKNORM_ERR_ALIGN;
+    if (num_slices < 1 || num_slices > kMaxSlices || segs[i]->width % num_slices != 0 ||
+        (segs[i]->width / num_slices) % ve != 0)
+      return QKNORM_ERR_SLICES;
+  }
+  if (!eps_ok(eps)) return QKNORM_ERR_EPS;
+  for (int i = 0; i < nseg; ++i) {
+    const Rows oi = flat(outs[i], T * 4);
+    for (int j = 0; j < nseg; ++j) {
+      if (overlap(oi, in_rows(*segs[j], dtype, T))) return QKNORM_ERR_ALIAS;
+      if (j != i && overlap(oi, flat(outs[j], T * 4))) return QKNORM_ERR_ALIAS;
+    }
+  }
+  int st = check_ctx(ctx);
+  if (st != QKNORM_OK) return st;
+
+  SegIn in[2];
+  for (int i = 0; i < nseg; ++i) in[i] = SegIn{segs[i]->width / ve, num_slices};
+  Plan plans[2];
+  int nw = 4;
+  st = plan_launch(ctx, in, nseg, T, plans, &nw);
+  if (st != QKNORM_OK) return st;
+  bool masked = false;
+  for (int i = 0; i < nseg; ++i) masked = masked || plans[i].masked;
+  qkn::Args a{};
+  a.T = T;
+  a.eps = eps;
+  int slots = 0;
+  for (int i = 0; i < nseg; ++i) {
+    qkn::Seg& s = a.seg[i];
+    s.x = segs[i]->x;
+    s.x_stride = segs[i]->x_stride;
+    s.stats_out = outs[i];
+    Plan pl = plans[i];
+    if (masked && !pl.masked) pl = Plan{pl.wpr_log2, pl.wpr_log2, plain_slots(in[i].nvec, pl.wpr_log2), true};
+    fill_layout(&s, pl, nw, in[i].nvec, num_slices, T);
+    s.h = static_cast<float>(segs[i]->width);
+    s.emit_rinv = 1;
+    slots = s.nslot > slots ? s.nslot : slots;
+  }
+  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(slots, nw), nw, masked, true, false};
+  if (v.vpl == 0) return QKNORM_ERR_SHAPE;
+  return run(ctx, v, a, nseg, stream);
+}
+
 int qknorm_partial_stats(qknorm_ctx* ctx, int dtype, int64_t T, const void* x_slice, int64_t x_stride,
                          int64_t slice_width, int slice_index, int num_slices, float* stats, void* stream) {
   if (!valid_dtype(dtype)) return QKNORM_ERR_DTYPE;

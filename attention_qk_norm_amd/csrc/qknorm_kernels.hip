@@ -13,8 +13,10 @@
 //   4. y = (x * r) * gamma (Eq. 1 order), rounded to the output type, stored
 //      with 16-byte vector stores; y may be x.
 // The split path reuses the same body: MODE_STATS stops after step 2 and
-// writes one fp32 per row (Algorithm 1, Phase A); MODE_APPLY skips step 2 and
-// combines precomputed partials instead (Phase B's scalar sum, then Phase C).
+// writes one fp32 per row (Algorithm 1, Phase A), or after step 3 and writes
+// the row's inverse RMS for a consumer that scales the row itself;
+// MODE_APPLY skips step 2 and combines precomputed partials instead (Phase
+// B's scalar sum, then Phase C). MODE_HEAD is the headwise form.
 //
 // No matrix cores: the work is a reduction and an elementwise scale, bound by
 // HBM bandwidth.
@@ -147,7 +149,7 @@ struct Hot {
   const float* stats_in;
   float* stats_out;
   int64_t x_stride, y_stride, T;
-  int rows_per_wg, nwg, nslot, wpr_log2, sub_log2, lds_gamma, lay_k, comb_k, slice_vec, head_log2;
+  int rows_per_wg, nwg, nslot, wpr_log2, sub_log2, lds_gamma, lay_k, comb_k, slice_vec, head_log2, emit_rinv;
   uint32_t row_bytes, flush_mask;
   float inv_slice_vec, h, inv_h, eps;
 
@@ -155,7 +157,7 @@ struct Hot {
       : x(s.x), y(s.y), gamma(s.gamma), stats_in(s.stats_in), stats_out(s.stats_out),
         x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
         nslot(s.nslot), wpr_log2(s.wpr_log2), sub_log2(s.sub_log2), lds_gamma(s.lds_gamma),
-        lay_k(s.lay_k), comb_k(s.comb_k), slice_vec(s.slice_vec), head_log2(s.head_log2),
+        lay_k(s.lay_k), comb_k(s.comb_k), slice_vec(s.slice_vec), head_log2(s.head_log2), emit_rinv(s.emit_rinv),
         row_bytes(s.row_bytes), flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h),
         inv_h(s.inv_h), eps(a.eps) {}
 };
@@ -281,11 +283,17 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
   return S;
 }
 
+// The inverse RMS of a row (review Eq. 6): the fused forward and the
+// statistic-only output use this same expression, so they agree bit for bit.
+__device__ __forceinline__ float inv_rms(float S, float h, float eps) {
+  return 1.0f / __builtin_sqrtf(S / h + eps);
+}
+
 template <class E, int VPL, bool NT>
 __device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const u32x4 (&g)[VPL], float S,
                                             float h, float eps, __amdgpu_buffer_rsrc_t yr,
                                             const Layout<VPL>& L) {
-  const float r = 1.0f / __builtin_sqrtf(S / h + eps);
+  const float r = inv_rms(S, h, eps);
 #pragma unroll
   for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::scale(d[j], g[j], r));
 }
@@ -306,7 +314,7 @@ __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const u32x4 (&
     S = row_stat<E, VPL, MASKED>(d, s, L, wave, lane, part);
   }
   if constexpr (MODE == MODE_STATS) {
-    if (live && L.tl == 0) s.stats_out[row] = S;
+    if (live && L.tl == 0) s.stats_out[row] = s.emit_rinv ? inv_rms(S, s.h, s.eps) : S;
   } else {
     scale_store<E, VPL, NT>(d, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
   }
@@ -539,7 +547,10 @@ hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hi
   } else if (v.mode == MODE_HEAD) {
     hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_HEAD, false, true, false>), gd, bd, lds, st, a);
   } else if (v.mode == MODE_STATS) {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, false, true, false>), gd, bd, lds, st, a);
+    if (v.masked)
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, true, true, false>), gd, bd, lds, st, a);
+    else
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, false, true, false>), gd, bd, lds, st, a);
   } else {
     hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_APPLY, false, true, false>), gd, bd, lds, st, a);
   }

@@ -29,7 +29,7 @@ namespace qkn {
 
 enum Mode : int {
   MODE_FWD = 0,    // statistic and scaling in one pass (row stays in registers)
-  MODE_STATS = 1,  // statistic only: one fp32 per row to `stats_out`
+  MODE_STATS = 1,  // statistic only: one fp32 per row to `stats_out` (S, or 1/RMS if emit_rinv)
   MODE_APPLY = 2,  // combine `comb_k` precomputed partials, then scale
   MODE_HEAD = 3,   // headwise: every head of 2^head_log2 vectors has its own statistic
 };
@@ -63,6 +63,7 @@ struct Seg {
   uint32_t flush_mask;    // segmented layout: bit j set when slot j ends a slice
   int32_t head_log2;      // HEAD: log2 of the 16-byte vectors per head (0 ... 6)
   float inv_h;            // HEAD: 1 / head width (a power of two, so exact)
+  int32_t emit_rinv;      // STATS: write 1 / sqrt(S / h + eps) instead of S
   int32_t slot_base[kMaxSlots];
   int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
 };
@@ -90,7 +91,7 @@ struct Variant {
   int mode;      // Mode
   int vpl;       // slots per lane the kernel is built for (>= what the segments need)
   int nw;        // wavefronts per workgroup: 4 or 16
-  bool masked;   // FWD only: masked layout
+  bool masked;   // FWD, STATS: masked layout
   bool nt;       // FWD only: non-temporal row loads and stores
   bool pipe;     // FWD only: persistent workgroups with the next rows prefetched
 };

@@ -168,6 +168,36 @@ int qknorm_forward_headwise(qknorm_ctx *ctx, int dtype, int64_t T,
                             int64_t head_dim, float eps, void *stream);
 
 /*
+ * The per-token inverse RMS alone, for a consumer that applies the scaling
+ * itself (review Eq. 6; the normalisation factors into a static weight and
+ * one dynamic scalar per token, which a later stage such as the rotary
+ * embedding or the attention kernel can fold in). For every token, over the
+ * query rows and the key rows in one launch:
+ *
+ *     rinv[t] = 1 / sqrt( S_t / width + eps ),
+ *
+ * S_t formed as qknorm_forward forms it (K slice partials added in
+ * ascending order). The value is bit for bit the factor qknorm_forward
+ * multiplies row t by: its output is (x * rinv) * gamma rounded once to the
+ * output type.
+ *
+ *   q, k        rows to read (only x, width and x_stride are used; k may be
+ *               NULL)
+ *   rinv_q, rinv_k  fp32 device arrays of T values (4-byte aligned); rinv_k
+ *               is ignored when k is NULL
+ *   dtype, T, eps, num_slices, stream: as for qknorm_forward
+ * Status, in validation order: QKNORM_ERR_DTYPE, QKNORM_ERR_SHAPE (T < 0;
+ * T == 0 returns QKNORM_OK), then for q and k in turn QKNORM_ERR_NULL,
+ * QKNORM_ERR_SHAPE, QKNORM_ERR_ALIGN, QKNORM_ERR_SLICES, then
+ * QKNORM_ERR_EPS, QKNORM_ERR_ALIAS (an output overlaps the rows or the other
+ * output), QKNORM_ERR_CONTEXT, QKNORM_ERR_DEVICE.
+ */
+int qknorm_inv_rms(qknorm_ctx *ctx, int dtype, int64_t T,
+                   const qknorm_rows *q, const qknorm_rows *k,
+                   float eps, int num_slices,
+                   float *rinv_q, float *rinv_k, void *stream);
+
+/*
  * Split path, step 1: one slice's partial sums of squares (Algorithm 1,
  * Phase A: a block-wide sum of the local shard's squares, published as one
  * scalar per token; review Eqs. 3-4).

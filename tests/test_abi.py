@@ -194,6 +194,42 @@ def test_headwise_validation(L):
         assert _head(L, **kw) == want, kw
 
 
+def _rinv(L, dtype=qk.BF16, T=64, q=None, k="default", rq=A + 40 * MB, rk=A + 41 * MB, eps=1e-6, K=1):
+    if q is None:
+        q = qk.Rows(A, 0, 4096, 4096, 4096)
+    if k == "default":
+        k = qk.Rows(A + 16 * MB, 0, 1024, 1024, 1024)
+    return L.qknorm_inv_rms(None, dtype, T, ctypes.byref(q), ctypes.byref(k) if k is not None else None,
+                            eps, K, rq, rk, None)
+
+
+def test_inv_rms_validation(L):
+    R = qk.Rows
+    assert _rinv(L) == qk.ERR_CONTEXT
+    assert _rinv(L, k=None, rk=None) == qk.ERR_CONTEXT
+    assert _rinv(L, K=64) == qk.ERR_CONTEXT
+    assert _rinv(L, T=0) == qk.OK
+    cases = [
+        (dict(dtype=5), qk.ERR_DTYPE),
+        (dict(T=-2), qk.ERR_SHAPE),
+        (dict(rq=None), qk.ERR_NULL),
+        (dict(rk=None), qk.ERR_NULL),
+        (dict(q=R(0, 0, 4096, 4096, 4096)), qk.ERR_NULL),
+        (dict(q=R(A, 0, 4096, 4000, 4096)), qk.ERR_SHAPE),
+        (dict(q=R(A + 8, 0, 4096, 4096, 4096)), qk.ERR_ALIGN),
+        (dict(rq=A + 40 * MB + 2), qk.ERR_ALIGN),
+        (dict(K=3), qk.ERR_SLICES),
+        (dict(eps=float("nan")), qk.ERR_EPS),
+        # an output inside the query rows, inside the key rows, or over the other output
+        (dict(rq=A + 1024), qk.ERR_ALIAS),
+        (dict(rk=A + 16 * MB + 4), qk.ERR_ALIAS),
+        (dict(rk=A + 40 * MB + 64), qk.ERR_ALIAS),
+        (dict(rk=A + 40 * MB + 256), qk.ERR_CONTEXT),  # just past T = 64 floats
+    ]
+    for kw, want in cases:
+        assert _rinv(L, **kw) == want, kw
+
+
 def _stats(L, dtype=qk.BF16, T=256, x=A, stride=5120, w=1280, s=0, K=4, st=A + 64 * MB):
     return L.qknorm_partial_stats(None, dtype, T, x, stride, w, s, K, st, None)
 

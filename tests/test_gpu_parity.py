@@ -448,3 +448,68 @@ def test_headwise_zero_heads_and_reproducibility():
     assert (y1[:, 2 * D:3 * D] == 0).all()
     ref, _ = oracle.qk_headwise(x, x, g, g, D, 1e-6)
     assert_parity(y1, ref, torch.bfloat16, "zero head")
+
+
+# ---- the per-token inverse RMS alone ------------------------------------------------
+
+def forward_from_rinv(x, r, g, dtype):
+    """(x * r) * gamma in fp32, rounded once to the output type: the fused
+    forward's arithmetic, given its factor r."""
+    y = (x.float() * r.cpu()[:, None]) * g.float()
+    return y.to(dtype)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_inv_rms_workloads(name):
+    """r_t against the oracle's Eq. 6 at fp32 tolerance, and bit for bit the
+    factor the fused forward applies (same K)."""
+    d = workloads.generate(name)
+    w = d["w"]
+    q, k = gpu(d["q"]), gpu(d["k"])
+    for K in w.slices:
+        say("inv_rms", name, "K=%d" % K)
+        rq, rk = qk.inv_rms(q, k, eps=w.eps, num_slices=K)
+        yq, yk = qk.forward(q, k, gpu(d["gamma_q"]), gpu(d["gamma_k"]), eps=w.eps, num_slices=K)
+        torch.cuda.synchronize()
+        for r, x, g, y, which in ((rq, d["q"], d["gamma_q"], yq, "q"), (rk, d["k"], d["gamma_k"], yk, "k")):
+            ref = oracle.inv_rms(x, w.eps, K)
+            assert_parity(r, ref, torch.float32, "%s rinv %s K=%d" % (name, which, K))
+            assert torch.equal(y.cpu(), forward_from_rinv(x, r, g, w.torch_dtype)), (name, which, K)
+        del yq, yk
+
+
+@pytest.mark.parametrize("dtype,T,Hq,Hk,K", [("bf16", 70, 4096, 4096, 64), ("bf16", 5, 1536, 1536, 48),
+                                            ("f32", 33, 1000, 8, 1), ("bf16", 3, 65536, 1024, 16),
+                                            ("f32", 9, 32768, 4, 1), ("bf16", 3000, 512, 128, 2)])
+def test_inv_rms_shapes(dtype, T, Hq, Hk, K):
+    """Narrow slices (masked layout), the widest rows, many rows per SIMD."""
+    q = workloads.random_rows(T, Hq, dtype, [T, Hq, 11], dist="laplace")
+    k = workloads.random_rows(T, Hk, dtype, [T, Hk, 12], scale=0.01)
+    say("inv_rms", dtype, T, Hq, Hk, K)
+    rq, rk = qk.inv_rms(gpu(q), gpu(k), eps=1e-6, num_slices=K)
+    torch.cuda.synchronize()
+    assert_parity(rq, oracle.inv_rms(q, 1e-6, K), torch.float32, "q")
+    assert_parity(rk, oracle.inv_rms(k, 1e-6, K), torch.float32, "k")
+
+
+def test_inv_rms_worked_example_and_strided_rows():
+    """Eq. 6 of the worked example (printed 0.6065), and rows read through a
+    strided view of a packed buffer with outputs placed by the caller."""
+    g = read_golden("swiftqk_worked_example.txt")
+    x = torch.tensor([g["x"]], dtype=torch.float32)
+    for K in (2, 1):
+        say("inv_rms worked example K=%d" % K)
+        r, _ = qk.inv_rms(gpu(x), eps=g["eps"][0], num_slices=K)
+        torch.cuda.synchronize()
+        assert abs(float(r[0]) - g["rms_inv"][0]) <= 0.5e-4
+        assert_parity(r, oracle.inv_rms(x, g["eps"][0], K), torch.float32, "Eq. 6")
+    T, Hq, Hk = 40, 2048, 512
+    qkv = gpu(workloads.random_rows(T, Hq + 2 * Hk, "bf16", 95))
+    out = torch.full((3, T), -1.0, device=DEV)
+    say("inv_rms strided")
+    qk.inv_rms(qkv[:, :Hq], qkv[:, Hq:Hq + Hk], out_q=out[0], out_k=out[2])
+    torch.cuda.synchronize()
+    host = qkv.cpu()
+    assert_parity(out[0], oracle.inv_rms(host[:, :Hq], 1e-6, 1), torch.float32, "q")
+    assert_parity(out[2], oracle.inv_rms(host[:, Hq:Hq + Hk], 1e-6, 1), torch.float32, "k")
+    assert (out[1] == -1.0).all()
