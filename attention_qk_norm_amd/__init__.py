@@ -20,7 +20,7 @@ import threading
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqknorm.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_SLICES, ERR_ALIGN, ERR_DTYPE, ERR_EPS, ERR_ALIAS, ERR_DEVICE, ERR_CONTEXT = (
     -1, -2, -3, -4, -5, -6, -7, -8, -9)
@@ -148,7 +148,16 @@ def _dtype_code(t):
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise TypeError("qknorm supports float32 and bfloat16 tensors, got %s" % t.dtype)
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
+    raise TypeError("qknorm supports float32, bfloat16 and float8_e4m3fn tensors, got %s" % t.dtype)
+
+
+def gamma_dtype(row_dtype):
+    """The weights' dtype for rows of `row_dtype`: bfloat16 for FP8 rows,
+    else the rows' own dtype."""
+    torch = _torch()
+    return torch.bfloat16 if row_dtype == torch.float8_e4m3fn else row_dtype
 
 
 def _rows_of(x, y):
@@ -194,9 +203,10 @@ def _qk_rows(q, k, gamma_q, gamma_k, gamma_width, out_q, out_k):
     for g, x in ((gamma_q, q), (gamma_k, k)):
         if x is None:
             continue
-        if g.dtype != x.dtype or g.dim() != 1 or g.shape[0] != gamma_width(x) or not g.is_contiguous():
-            raise ValueError("gamma must be a contiguous 1-D tensor of the rows' dtype with %d weights"
-                             % gamma_width(x))
+        if g.dtype != gamma_dtype(x.dtype) or g.dim() != 1 or g.shape[0] != gamma_width(x) or \
+                not g.is_contiguous():
+            raise ValueError("gamma must be a contiguous 1-D %s tensor with %d weights"
+                             % (gamma_dtype(x.dtype), gamma_width(x)))
     return dt, T, rq, rk, out_q, out_k
 
 
@@ -296,8 +306,9 @@ def apply_stats(x_slice, gamma_slice, stats, h_total, eps=1e-6, out=None, ctx=No
     r = _rows_of(x_slice, out)
     if stats.dtype != torch.float32 or stats.dim() != 2 or stats.shape[1] != T or not stats.is_contiguous():
         raise ValueError("stats must be a contiguous float32 [K, T] tensor")
-    if gamma_slice.dtype != x_slice.dtype or gamma_slice.dim() != 1 or not gamma_slice.is_contiguous():
-        raise ValueError("gamma_slice must be a contiguous 1-D tensor of the rows' dtype")
+    if gamma_slice.dtype != gamma_dtype(x_slice.dtype) or gamma_slice.dim() != 1 or \
+            not gamma_slice.is_contiguous():
+        raise ValueError("gamma_slice must be a contiguous 1-D %s tensor" % gamma_dtype(x_slice.dtype))
     c = _ctx_of(x_slice, ctx)
     st = lib().qknorm_apply_stats(c.handle, dt, T, ctypes.byref(r), gamma_slice.data_ptr(),
                                   stats.data_ptr(), stats.shape[0], int(h_total), float(eps),

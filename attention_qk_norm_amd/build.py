@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqknorm.so")
-SOURCES = [os.path.join(CSRC, "qknorm_kernels.hip"), os.path.join(CSRC, "qknorm_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("qknorm_kernels_f32.hip", "qknorm_kernels_bf16.hip",
+                                            "qknorm_kernels_fp8.hip", "qknorm_launch.cpp", "qknorm_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -19,7 +20,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wextra",
     # keep the compiler from forming packed fp32 arithmetic (v_pk_*_f32)
@@ -30,17 +30,33 @@ FLAGS = [
 
 
 def build(out=LIB, extra=(), verbose=False):
-    """Compile every HIP source into `out` (always recompiles)."""
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    """Compile every HIP source (always, in parallel: one object per source)
+    and link them into `out`."""
+    tag = "%s.tmp%d" % (out, os.getpid())
+    objs = [tag + ".%d.o" % i for i in range(len(SOURCES))]
+    procs = []
     try:
+        for src, obj in zip(SOURCES, objs):
+            cmd = [HIPCC, *FLAGS, *extra, "-c", "-x", "hip", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd)))
+        failed = [src for src, p in procs if p.wait() != 0]
+        if failed:
+            raise RuntimeError("hipcc failed for " + ", ".join(failed))
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tag]
+        if verbose:
+            print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        os.replace(tmp, out)
+        os.replace(tag, out)
     finally:
-        if os.path.exists(tmp):
-            os.remove(tmp)
+        for _, p in procs:
+            if p.poll() is None:
+                p.kill()
+                p.wait()
+        for f in objs + [tag]:
+            if os.path.exists(f):
+                os.remove(f)
     return out
 
 

@@ -21,14 +21,14 @@ namespace {
 
 constexpr int64_t kVecBytes = 16;
 constexpr int kMaxSlices = 64;
-constexpr int kMaxSlots4 = 16;   // slots per lane, 4-wavefront workgroups
-constexpr int kMaxSlots16 = 8;   // slots per lane, 16-wavefront workgroups
 constexpr int64_t kMaxRows = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxTotalWidth = int64_t{1} << 24;  // exact as a float divisor
 
-int elem_bytes(int dtype) { return dtype == QKNORM_F32 ? 4 : 2; }
+int elem_bytes(int dtype) { return dtype == QKNORM_F32 ? 4 : dtype == QKNORM_BF16 ? 2 : 1; }
+// gamma is bf16 for fp8 rows, else the rows' own type
+int gamma_elem_bytes(int dtype) { return dtype == QKNORM_FP8_E4M3 ? 2 : elem_bytes(dtype); }
 int64_t vec_elems(int dtype) { return kVecBytes / elem_bytes(dtype); }
-bool valid_dtype(int dtype) { return dtype == QKNORM_F32 || dtype == QKNORM_BF16; }
+bool valid_dtype(int dtype) { return dtype == QKNORM_F32 || dtype == QKNORM_BF16 || dtype == QKNORM_FP8_E4M3; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -134,13 +134,13 @@ int check_fused(int dtype, int64_t T, const qknorm_rows* const* segs, const void
     }
   }
   if (!eps_ok(eps)) return QKNORM_ERR_EPS;
-  const int eb = elem_bytes(dtype);
+  const int geb = gamma_elem_bytes(dtype);
   for (int i = 0; i < nseg; ++i) {
     if (!in_out_ok(*segs[i], dtype, T)) return QKNORM_ERR_ALIAS;
     const Rows yi = out_rows(*segs[i], dtype, T);
     for (int j = 0; j < nseg; ++j) {
       const int64_t gw = headwise ? head_dim : segs[j]->width;
-      if (overlap(yi, flat(gammas[j], gw * eb))) return QKNORM_ERR_ALIAS;
+      if (overlap(yi, flat(gammas[j], gw * geb))) return QKNORM_ERR_ALIAS;
       if (j == i) continue;
       if (overlap(yi, in_rows(*segs[j], dtype, T)) || overlap(yi, out_rows(*segs[j], dtype, T)))
         return QKNORM_ERR_ALIAS;
@@ -191,6 +191,13 @@ bool plan_segment(int64_t nvec, int K, int max_wl, int cap, int forced_wl, Plan*
   const int hi = forced_wl >= 0 ? forced_wl : max_wl;
   for (int wl = lo; wl <= hi; ++wl) {
     const Plan p = seg_plan(slice_vec, K, wl);
+    // slices much narrower than a sub-team leave most of each slot's lanes
+    // empty: the masked layout then issues half the loads or fewer
+    const int m = plain_slots(nvec, wl);
+    if (m <= cap && 2 * m <= p.slots) {
+      *out = Plan{wl, wl, m, true};
+      return true;
+    }
     if (p.slots <= cap) {
       *out = p;
       return true;
@@ -237,17 +244,18 @@ struct SegIn {
 //    16384 x 4096, no slower on the grouped-query shape);
 //  - in between, every row's loads are issued in the first round, and one
 //    wavefront per row is fastest.
-int plan_launch(const qknorm_ctx* ctx, const SegIn* in, int nseg, int64_t T, Plan* plans, int* nw) {
+int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int64_t T, Plan* plans, int* nw) {
+  const int cap4 = qkn::max_slots(dtype, 4), cap16 = qkn::max_slots(dtype, 16);
   const int fl = forced_log2(ctx);
   bool ok = true;
   bool wide = fl > 2;
   if (!wide) {
-    for (int i = 0; i < nseg && ok; ++i) ok = plan_segment(in[i].nvec, in[i].K, 2, kMaxSlots4, fl, &plans[i]);
+    for (int i = 0; i < nseg && ok; ++i) ok = plan_segment(in[i].nvec, in[i].K, 2, cap4, fl, &plans[i]);
     if (!ok) wide = fl < 0;  // retry with 16-wavefront workgroups
   }
   if (wide) {
     ok = true;
-    for (int i = 0; i < nseg && ok; ++i) ok = plan_segment(in[i].nvec, in[i].K, 4, kMaxSlots16, fl, &plans[i]);
+    for (int i = 0; i < nseg && ok; ++i) ok = plan_segment(in[i].nvec, in[i].K, 4, cap16, fl, &plans[i]);
     *nw = 16;
     return ok ? QKNORM_OK : QKNORM_ERR_SHAPE;
   }
@@ -260,7 +268,7 @@ int plan_launch(const qknorm_ctx* ctx, const SegIn* in, int nseg, int64_t T, Pla
         if (plans[i].wpr_log2 != 0) continue;
         const Plan p = plans[i].masked ? Plan{1, 1, plain_slots(in[i].nvec, 1), true}
                                        : seg_plan(in[i].nvec / in[i].K, in[i].K, 1);
-        if (p.slots <= kMaxSlots4) plans[i] = p;
+        if (p.slots <= cap4) plans[i] = p;
       }
       return QKNORM_OK;
     }
@@ -326,10 +334,15 @@ void fill_layout(qkn::Seg* s, const Plan& p, int nw, int64_t nvec, int K, int64_
   }
 }
 
+// Bytes of the weights of one row of `row_bytes` bytes.
+uint32_t gamma_bytes(uint32_t row_bytes, int dtype) {
+  return row_bytes / static_cast<uint32_t>(elem_bytes(dtype)) * static_cast<uint32_t>(gamma_elem_bytes(dtype));
+}
+
 // Several rows per workgroup share one copy of gamma staged in LDS.
 constexpr uint32_t kLdsGammaMax = 32768;
-void share_gamma(qkn::Seg* s) {
-  s->lds_gamma = (s->rows_per_wg > 1 && s->row_bytes <= kLdsGammaMax) ? 1 : 0;
+void share_gamma(qkn::Seg* s, int dtype) {
+  s->lds_gamma = (s->rows_per_wg > 1 && gamma_bytes(s->row_bytes, dtype) <= kLdsGammaMax) ? 1 : 0;
 }
 
 // Enqueue `nseg` segments: grid.x covers the larger segment (capped by the
@@ -342,7 +355,7 @@ int run(const qknorm_ctx* ctx, qkn::Variant v, const qkn::Args& a, int nseg, voi
     gx = a.seg[i].nwg > gx ? a.seg[i].nwg : gx;
     // whole chunks of one 16-byte vector per thread (see the kernel's gamma_to_lds)
     const unsigned chunk = 16u * 64u * static_cast<unsigned>(v.nw);
-    const unsigned need = (a.seg[i].row_bytes + chunk - 1) / chunk * chunk;
+    const unsigned need = (gamma_bytes(a.seg[i].row_bytes, v.dtype) + chunk - 1) / chunk * chunk;
     if (a.seg[i].lds_gamma && need > lds) lds = need;
   }
   if (gx <= 0) return QKNORM_OK;
@@ -384,7 +397,7 @@ const char* qknorm_status_string(int status) {
 
 int64_t qknorm_max_width(int dtype) {
   if (!valid_dtype(dtype)) return 0;
-  return int64_t{64} * 16 * kMaxSlots16 * vec_elems(dtype);
+  return int64_t{64} * 16 * qkn::max_slots(dtype, 16) * vec_elems(dtype);
 }
 
 int qknorm_create_ex(qknorm_ctx** ctx_out, int device, const qknorm_options* opts) {
@@ -434,7 +447,7 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
   for (int i = 0; i < nseg; ++i) in[i] = SegIn{segs[i]->width / ve, num_slices};
   Plan plans[2];
   int nw = 4;
-  st = plan_launch(ctx, in, nseg, T, plans, &nw);
+  st = plan_launch(ctx, dtype, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) return st;
 
   bool masked = false;
@@ -455,12 +468,12 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
     Plan pl = plans[i];
     if (masked && !pl.masked) pl = Plan{pl.wpr_log2, pl.wpr_log2, plain_slots(in[i].nvec, pl.wpr_log2), true};
     fill_layout(&s, pl, nw, in[i].nvec, num_slices, T);
-    share_gamma(&s);
+    share_gamma(&s, dtype);
     s.h = static_cast<float>(segs[i]->width);
     s.comb_k = 0;
     slots = s.nslot > slots ? s.nslot : slots;
   }
-  qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw), nw, masked,
+  qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw, dtype), nw, masked,
                  ctx->opt.cached_rows == 0 || masked, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, nseg, stream);
@@ -485,7 +498,7 @@ int qknorm_forward_headwise(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_
   for (int i = 0; i < nseg; ++i) in[i] = SegIn{segs[i]->width / ve, 1};
   Plan plans[2];
   int nw = 4;
-  st = plan_launch(ctx, in, nseg, T, plans, &nw);
+  st = plan_launch(ctx, dtype, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) return st;
   const int hv = head_vectors(head_dim, dtype);
   int hl = 0;
@@ -509,7 +522,7 @@ int qknorm_forward_headwise(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_
     s.inv_h = 1.0f / static_cast<float>(head_dim);
     slots = s.nslot > slots ? s.nslot : slots;
   }
-  qkn::Variant v{dtype, qkn::MODE_HEAD, qkn::compiled_vpl(slots, nw), nw, false, true, false};
+  qkn::Variant v{dtype, qkn::MODE_HEAD, qkn::compiled_vpl(slots, nw, dtype), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, nseg, stream);
 }
@@ -548,7 +561,7 @@ int qknorm_inv_rms(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
   for (int i = 0; i < nseg; ++i) in[i] = SegIn{segs[i]->width / ve, num_slices};
   Plan plans[2];
   int nw = 4;
-  st = plan_launch(ctx, in, nseg, T, plans, &nw);
+  st = plan_launch(ctx, dtype, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) return st;
   bool masked = false;
   for (int i = 0; i < nseg; ++i) masked = masked || plans[i].masked;
@@ -568,7 +581,7 @@ int qknorm_inv_rms(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
     s.emit_rinv = 1;
     slots = s.nslot > slots ? s.nslot : slots;
   }
-  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(slots, nw), nw, masked, true, false};
+  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(slots, nw, dtype), nw, masked, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, nseg, stream);
 }
@@ -595,7 +608,7 @@ int qknorm_partial_stats(qknorm_ctx* ctx, int dtype, int64_t T, const void* x_sl
   const SegIn in{nvec, 1};
   Plan plan;
   int nw = 4;
-  st = plan_launch(ctx, &in, 1, T, &plan, &nw);
+  st = plan_launch(ctx, dtype, &in, 1, T, &plan, &nw);
   if (st != QKNORM_OK) return st;
   qkn::Args a{};
   a.T = T;
@@ -606,7 +619,7 @@ int qknorm_partial_stats(qknorm_ctx* ctx, int dtype, int64_t T, const void* x_sl
   s.stats_out = out;
   fill_layout(&s, plan, nw, nvec, 1, T);
   s.h = static_cast<float>(slice_width);
-  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(s.nslot, nw), nw, false, true, false};
+  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(s.nslot, nw, dtype), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, 1, stream);
 }
@@ -625,10 +638,9 @@ int qknorm_apply_stats(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows*
   if ((reinterpret_cast<uintptr_t>(stats) & 3u) != 0) return QKNORM_ERR_ALIGN;
   if (num_slices < 1 || num_slices > kMaxSlices) return QKNORM_ERR_SLICES;
   if (!eps_ok(eps)) return QKNORM_ERR_EPS;
-  const int eb = elem_bytes(dtype);
   const Rows yr = out_rows(*x_slice, dtype, T);
   if (!in_out_ok(*x_slice, dtype, T) || overlap(yr, flat(stats, num_slices * T * 4)) ||
-      overlap(yr, flat(gamma_slice, x_slice->width * eb)))
+      overlap(yr, flat(gamma_slice, x_slice->width * gamma_elem_bytes(dtype))))
     return QKNORM_ERR_ALIAS;
   st = check_ctx(ctx);
   if (st != QKNORM_OK) return st;
@@ -637,7 +649,7 @@ int qknorm_apply_stats(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows*
   const SegIn in{nvec, 1};
   Plan plan;
   int nw = 4;
-  st = plan_launch(ctx, &in, 1, T, &plan, &nw);
+  st = plan_launch(ctx, dtype, &in, 1, T, &plan, &nw);
   if (st != QKNORM_OK) return st;
   qkn::Args a{};
   a.T = T;
@@ -650,10 +662,10 @@ int qknorm_apply_stats(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows*
   s.x_stride = x_slice->x_stride;
   s.y_stride = x_slice->y_stride;
   fill_layout(&s, plan, nw, nvec, 1, T);
-  share_gamma(&s);
+  share_gamma(&s, dtype);
   s.comb_k = num_slices;
   s.h = static_cast<float>(h_total);
-  qkn::Variant v{dtype, qkn::MODE_APPLY, qkn::compiled_vpl(s.nslot, nw), nw, false, true, false};
+  qkn::Variant v{dtype, qkn::MODE_APPLY, qkn::compiled_vpl(s.nslot, nw, dtype), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, 1, stream);
 }

@@ -1,4 +1,8 @@
-// qknorm_kernels.hip -- gfx950 kernels for layerwise QK-Norm.
+// qknorm_kernels.h -- gfx950 kernels for layerwise QK-Norm (device templates).
+//
+// Each element type is instantiated in a translation unit of its own
+// (qknorm_kernels_f32.hip, _bf16.hip, _fp8.hip), so the three compile in
+// parallel.
 //
 // Per row (SwiftQK technical review, Eq. 1; the K-slice statistic of section
 // 4b, Eqs. 3-6):
@@ -20,6 +24,8 @@
 //
 // No matrix cores: the work is a reduction and an elementwise scale, bound by
 // HBM bandwidth.
+#pragma once
+
 #include "qknorm_launch.h"
 
 #include "qknorm.h"
@@ -56,8 +62,23 @@ __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, 
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, NT ? 2 : 0);
 }
 
+// Weights stored in the rows' own type: one 16-byte weight vector per row
+// vector, at the same byte offset.
+struct SameTypeGamma {
+  using G = u32x4;
+  static constexpr uint32_t kGammaScale = 1;  // weight bytes per row byte
+  static __device__ __forceinline__ G load_gamma(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return load16<false>(r, off);
+  }
+  static __device__ __forceinline__ G gamma_lds(const u32x4* lds, uint32_t v) { return lds[v]; }
+  // fp32 and bf16 results cannot leave their type's range here
+  template <int V>
+  static __device__ __forceinline__ bool may_saturate(const G (&)[V], float) { return false; }
+};
+
 // binary32 rows: 4 elements per 16-byte vector.
-struct F32 {
+struct F32 : SameTypeGamma {
+  static constexpr int kDtype = QKNORM_F32;
   static constexpr int kBytes = 4;
   static __device__ __forceinline__ float sumsq(u32x4 d, float acc) {
 #pragma unroll
@@ -67,6 +88,7 @@ struct F32 {
     }
     return acc;
   }
+  template <bool SAT>
   static __device__ __forceinline__ u32x4 scale(u32x4 d, u32x4 g, float r) {
     u32x4 o;
 #pragma unroll
@@ -85,7 +107,8 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_c
 // sums use the bf16 dot-product instruction (fp32 result and accumulator);
 // the scaling widens to fp32 and rounds back to nearest-even in one packed
 // conversion.
-struct BF16 {
+struct BF16 : SameTypeGamma {
+  static constexpr int kDtype = QKNORM_BF16;
   static constexpr int kBytes = 2;
   static __device__ __forceinline__ float sumsq(u32x4 d, float acc) {
 #pragma unroll
@@ -95,6 +118,7 @@ struct BF16 {
     }
     return acc;
   }
+  template <bool SAT>
   static __device__ __forceinline__ u32x4 scale(u32x4 d, u32x4 g, float r) {
     u32x4 o;
 #pragma unroll
@@ -105,6 +129,114 @@ struct BF16 {
       const float gh = __uint_as_float(g[i] & 0xffff0000u);
       const f32x2 yv = {xl * r * gl, xh * r * gh};
       o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(yv, bf16x2));
+    }
+    return o;
+  }
+};
+
+// OCP FP8 E4M3 rows (the e4m3 encoding without infinities that gfx950
+// converts natively; largest finite value 448): 16 elements per 16-byte
+// vector. The weights stay bfloat16, so one row vector takes two weight
+// vectors, at twice the row vector's byte offset. Squares accumulate in fp32
+// (review section 5); y = (x * r) * gamma in fp32 is rounded to nearest-even
+// e4m3, saturating at +-448 (the conversion instruction alone would give NaN
+// past 464), while NaN stays NaN.
+__device__ __forceinline__ f32x2 fp8_pair(uint32_t w, bool high) {
+  return high ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true)
+              : __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+}
+
+// The raw word, hidden from the optimiser: the scaling pass decodes the row
+// again instead of keeping 16 decoded floats per vector alive across the
+// reduction (which costs about 12 more VGPRs per slot than the decode
+// costs in instructions). The empty asm emits nothing.
+__device__ __forceinline__ uint32_t opaque(uint32_t w) {
+  asm volatile("" : "+v"(w));
+  return w;
+}
+
+__device__ __forceinline__ float sat_e4m3(float v) {
+  return __builtin_fabsf(v) > 448.0f ? __builtin_copysignf(448.0f, v) : v;
+}
+
+struct FP8 {
+  static constexpr int kDtype = QKNORM_FP8_E4M3;
+  static constexpr int kBytes = 1;
+  struct G {
+    u32x4 lo, hi;  // weights of elements 0-7 and 8-15 of the row vector
+  };
+  static constexpr uint32_t kGammaScale = 2;
+  static __device__ __forceinline__ G load_gamma(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const uint32_t o = off == kOutside ? kOutside : 2u * off;
+    return G{load16<false>(r, o), load16<false>(r, o == kOutside ? kOutside : o + 16u)};
+  }
+  static __device__ __forceinline__ G gamma_lds(const u32x4* lds, uint32_t v) {
+    return G{lds[2u * v], lds[2u * v + 1u]};
+  }
+  static __device__ __forceinline__ float sumsq(u32x4 d, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 a = fp8_pair(d[i], false);
+      const f32x2 b = fp8_pair(d[i], true);
+      acc = __builtin_fmaf(a.x, a.x, acc);
+      acc = __builtin_fmaf(a.y, a.y, acc);
+      acc = __builtin_fmaf(b.x, b.x, acc);
+      acc = __builtin_fmaf(b.y, b.y, acc);
+    }
+    return acc;
+  }
+  // Can any result of this wavefront pass 448? |x_j r| <= sqrt(h) because
+  // x_j^2 <= S (fp32 rounding of S and of the products stays far inside the
+  // 2^-10 margin), so |y_j| <= sqrt(h) * max|gamma|. When even that bound
+  // stays below 448 the clamp is skipped. The largest |gamma| is taken on
+  // the bf16 bits (non-negative bf16 values order like 16-bit integers; a
+  // NaN weight counts as huge), one packed integer max per weight dword.
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  // by value, for the same reason as as_bf16x2
+  static __device__ __forceinline__ u16x2 magnitudes(uint32_t w) {
+    return __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+  }
+  template <int V>
+  static __device__ __forceinline__ bool may_saturate(const G (&g)[V], float h) {
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = __builtin_elementwise_max(m, magnitudes(g[j].lo[i]));
+        m = __builtin_elementwise_max(m, magnitudes(g[j].hi[i]));
+      }
+    }
+    const uint32_t top = m.x > m.y ? m.x : m.y;
+    const float gmax = __uint_as_float(top << 16);
+    const bool lane = !(gmax * __builtin_sqrtf(h) * (1.0f + 0x1p-10f) <= 448.0f);
+    return __builtin_amdgcn_ballot_w64(lane) != 0;
+  }
+  template <bool SAT>
+  static __device__ __forceinline__ u32x4 scale(u32x4 d, const G& g, float r) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // row dword i holds elements 4i..4i+3; their weights are bf16 words
+      // 4i..4i+3, i.e. weight dwords 2i and 2i+1
+      const uint32_t g0 = i < 2 ? g.lo[2 * i] : g.hi[2 * i - 4];
+      const uint32_t g1 = i < 2 ? g.lo[2 * i + 1] : g.hi[2 * i - 3];
+      const uint32_t w8 = opaque(d[i]);
+      const f32x2 a = fp8_pair(w8, false);
+      const f32x2 b = fp8_pair(w8, true);
+      float y0 = a.x * r * __uint_as_float(g0 << 16);
+      float y1 = a.y * r * __uint_as_float(g0 & 0xffff0000u);
+      float y2 = b.x * r * __uint_as_float(g1 << 16);
+      float y3 = b.y * r * __uint_as_float(g1 & 0xffff0000u);
+      if constexpr (SAT) {
+        y0 = sat_e4m3(y0);
+        y1 = sat_e4m3(y1);
+        y2 = sat_e4m3(y2);
+        y3 = sat_e4m3(y3);
+      }
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+      o[i] = static_cast<uint32_t>(w);
     }
     return o;
   }
@@ -217,6 +349,15 @@ __device__ __forceinline__ void load_row(u32x4 (&d)[VPL], __amdgpu_buffer_rsrc_t
   for (int j = 0; j < VPL; ++j) d[j] = load16<NT>(r, L.off[j]);
 }
 
+// The weights of this lane's slots, straight from memory (L2 after the
+// first row).
+template <class E, int VPL>
+__device__ __forceinline__ void load_gamma(typename E::G (&g)[VPL], const Hot& s, const Layout<VPL>& L) {
+  const auto r = rsrc(s.gamma, s.row_bytes * E::kGammaScale);
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) g[j] = E::load_gamma(r, L.off[j]);
+}
+
 // The row statistic S = sum over slices (ascending) of each slice's sum of
 // squares. Teams of several wavefronts add their partials through `part`
 // (one barrier); every lane of the team returns the same S.
@@ -289,19 +430,27 @@ __device__ __forceinline__ float inv_rms(float S, float h, float eps) {
   return 1.0f / __builtin_sqrtf(S / h + eps);
 }
 
-template <class E, int VPL, bool NT>
-__device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const u32x4 (&g)[VPL], float S,
+// BOUNDED: S covers every element scaled here (not so for partials handed in
+// by a caller), so |x r| <= sqrt(h) and the weights alone decide whether a
+// result can saturate.
+template <class E, int VPL, bool NT, bool BOUNDED>
+__device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], float S,
                                             float h, float eps, __amdgpu_buffer_rsrc_t yr,
                                             const Layout<VPL>& L) {
   const float r = inv_rms(S, h, eps);
+  if (!BOUNDED || E::may_saturate(g, h)) {
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::scale(d[j], g[j], r));
+    for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::template scale<true>(d[j], g[j], r));
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::template scale<false>(d[j], g[j], r));
+  }
 }
 
 // Finish one row whose data (and weights) are in registers: statistic (or
 // the precomputed partials), then scale and store, or publish the statistic.
 template <class E, int VPL, int MODE, bool MASKED, bool NT>
-__device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const u32x4 (&g)[VPL], const Hot& s,
+__device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], const Hot& s,
                                            const Layout<VPL>& L, int64_t row, bool live, int wave,
                                            int lane, float* part) {
   float S = 0.f;
@@ -316,7 +465,8 @@ __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const u32x4 (&
   if constexpr (MODE == MODE_STATS) {
     if (live && L.tl == 0) s.stats_out[row] = s.emit_rinv ? inv_rms(S, s.h, s.eps) : S;
   } else {
-    scale_store<E, VPL, NT>(d, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
+    scale_store<E, VPL, NT, MODE != MODE_APPLY>(d, g, S, s.h, s.eps,
+                                                row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
   }
 }
 
@@ -362,17 +512,22 @@ __device__ __forceinline__ void head_sums(float (&q)[V], int hl, int lane) {
 // (the mean divides by the head width) and the head's weights `g`, which
 // are the same vector for every slot of this lane.
 template <class E, int VPL, bool NT>
-__device__ __forceinline__ void head_finish(const u32x4 (&d)[VPL], u32x4 g, const Hot& s,
+__device__ __forceinline__ void head_finish(const u32x4 (&d)[VPL], const typename E::G& g, const Hot& s,
                                             const Layout<VPL>& L, int64_t row, bool live, int lane) {
   float q[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) q[j] = E::sumsq(d[j], 0.f);
   head_sums<VPL>(q, s.head_log2, lane);
   const auto yr = row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes);
+  const typename E::G gs[1] = {g};
+  if (E::may_saturate(gs, s.h)) {
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) {
-    const float r = 1.0f / __builtin_sqrtf(q[j] * s.inv_h + s.eps);
-    store16<NT>(yr, L.off[j], E::scale(d[j], g, r));
+    for (int j = 0; j < VPL; ++j)
+      store16<NT>(yr, L.off[j], E::template scale<true>(d[j], g, 1.0f / __builtin_sqrtf(q[j] * s.inv_h + s.eps)));
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      store16<NT>(yr, L.off[j], E::template scale<false>(d[j], g, 1.0f / __builtin_sqrtf(q[j] * s.inv_h + s.eps)));
   }
 }
 
@@ -384,12 +539,14 @@ __device__ __forceinline__ void head_finish(const u32x4 (&d)[VPL], u32x4 g, cons
 // (gamma_from_lds), so it overlaps the row transfer. The LDS block is
 // rounded up to whole NW * 64 * 16-byte chunks, so lanes past the end of
 // gamma (which read zeros) still write inside it.
-template <int VPL, int NW>
+template <class E, int VPL, int NW>
 __device__ __forceinline__ void gamma_to_lds(const Hot& s, int wave, int lane, u32x4* lds_g) {
-  // rows_per_wg > 1 here, so a row has at most VPL * NW * 64 / 2 vectors
-  constexpr int kChunks = (VPL + 1) / 2;
-  const auto gr = rsrc(s.gamma, s.row_bytes);
-  const uint32_t nvec = s.row_bytes >> 4;
+  // rows_per_wg > 1 here, so a row has at most VPL * NW * 64 / 2 vectors,
+  // and its weights kGammaScale times as many
+  constexpr int kChunks = static_cast<int>(E::kGammaScale) * ((VPL + 1) / 2);
+  const uint32_t gbytes = s.row_bytes * E::kGammaScale;
+  const auto gr = rsrc(s.gamma, gbytes);
+  const uint32_t nvec = gbytes >> 4;
 #pragma unroll
   for (int k = 0; k < kChunks; ++k) {
     const uint32_t v0 = static_cast<uint32_t>(wave * kWave + k * NW * kWave);
@@ -401,13 +558,14 @@ __device__ __forceinline__ void gamma_to_lds(const Hot& s, int wave, int lane, u
 
 // Wait for this wavefront's copies (issued before its VPL row loads, so at
 // most VPL loads may stay in flight), then for the whole workgroup's.
-template <int VPL>
-__device__ __forceinline__ void gamma_from_lds(u32x4 (&g)[VPL], const Layout<VPL>& L, const u32x4* lds_g) {
+template <class E, int VPL>
+__device__ __forceinline__ void gamma_from_lds(typename E::G (&g)[VPL], const Layout<VPL>& L,
+                                               const u32x4* lds_g) {
   // s_waitcnt with vmcnt = VPL and the lgkm / exp counters left alone
   __builtin_amdgcn_s_waitcnt((VPL & 0xF) | ((VPL >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) g[j] = lds_g[L.off[j] == kOutside ? 0u : (L.off[j] >> 4)];
+  for (int j = 0; j < VPL; ++j) g[j] = E::gamma_lds(lds_g, L.off[j] == kOutside ? 0u : (L.off[j] >> 4));
 }
 
 // Persistent workgroups: group gi, gi + G, gi + 2G, ... (G = gridDim.x). The
@@ -421,22 +579,23 @@ __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L
   const int G = gridDim.x;
   int g0 = blockIdx.x;
   if (g0 >= s.nwg) return;
-  u32x4 A[VPL], B[VPL], g[VPL];
+  u32x4 A[VPL], B[VPL];
+  typename E::G g[VPL];
   int64_t ra = static_cast<int64_t>(g0) * s.rows_per_wg + L.team;
   load_row<E, VPL, NT>(A, row_rsrc<E>(s.x, s.x_stride, ra, ra < s.T, s.row_bytes), L);
-  load_row<E, VPL, false>(g, rsrc(s.gamma, s.row_bytes), L);
+  load_gamma<E, VPL>(g, s, L);
   for (;;) {
     const int g1 = g0 + G;
     const int64_t rb = static_cast<int64_t>(g1) * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(B, row_rsrc<E>(s.x, s.x_stride, rb, g1 < s.nwg && rb < s.T, s.row_bytes), L);
     float S = row_stat<E, VPL, MASKED>(A, s, L, wave, lane, part);
-    scale_store<E, VPL, NT>(A, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, ra, ra < s.T, s.row_bytes), L);
+    scale_store<E, VPL, NT, true>(A, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, ra, ra < s.T, s.row_bytes), L);
     if (g1 >= s.nwg) break;
     const int g2 = g1 + G;
     ra = static_cast<int64_t>(g2) * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(A, row_rsrc<E>(s.x, s.x_stride, ra, g2 < s.nwg && ra < s.T, s.row_bytes), L);
     S = row_stat<E, VPL, MASKED>(B, s, L, wave, lane, part);
-    scale_store<E, VPL, NT>(B, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, rb, rb < s.T, s.row_bytes), L);
+    scale_store<E, VPL, NT, true>(B, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, rb, rb < s.T, s.row_bytes), L);
     if (g2 >= s.nwg) break;
     g0 = g2;
   }
@@ -451,8 +610,8 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
     int64_t row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
     u32x4 d[V];
     load_row<E, V, NT>(d, row_rsrc<E>(s.x, s.x_stride, row, row < s.T, s.row_bytes), L);
-    const u32x4 g = load16<false>(rsrc(s.gamma, 16u << s.head_log2),
-                                  static_cast<uint32_t>(lane & ((1 << s.head_log2) - 1)) * 16u);
+    const typename E::G g = E::load_gamma(rsrc(s.gamma, (16u << s.head_log2) * E::kGammaScale),
+                                          static_cast<uint32_t>(lane & ((1 << s.head_log2) - 1)) * 16u);
     head_finish<E, V, NT>(d, g, s, L, row, row < s.T, lane);
     for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
       row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
@@ -468,15 +627,16 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
     int gi = blockIdx.x;
     int64_t row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
     bool live = row < s.T;
-    u32x4 d[V], g[V];
+    u32x4 d[V];
+    typename E::G g[V];
     const bool staged = MODE != MODE_STATS && s.lds_gamma;
-    if (staged) gamma_to_lds<V, NW>(s, wave, lane, lds_g);
+    if (staged) gamma_to_lds<E, V, NW>(s, wave, lane, lds_g);
     load_row<E, V, NT>(d, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
     if constexpr (MODE != MODE_STATS) {
       if (staged)
-        gamma_from_lds<V>(g, L, lds_g);
+        gamma_from_lds<E, V>(g, L, lds_g);
       else
-        load_row<E, V, false>(g, rsrc(s.gamma, s.row_bytes), L);
+        load_gamma<E, V>(g, s, L);
     }
     row_finish<E, V, MODE, MASKED, NT>(d, g, s, L, row, live, wave, lane, part);
     // Only grids capped at the hardware limit get here. Reloading gamma each
@@ -485,9 +645,10 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
     for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
       row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
       live = row < s.T;
-      u32x4 d2[V], g2[V];
+      u32x4 d2[V];
+      typename E::G g2[V];
       load_row<E, V, NT>(d2, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
-      if constexpr (MODE != MODE_STATS) load_row<E, V, false>(g2, rsrc(s.gamma, s.row_bytes), L);
+      if constexpr (MODE != MODE_STATS) load_gamma<E, V>(g2, s, L);
       row_finish<E, V, MODE, MASKED, NT>(d2, g2, s, L, row, live, wave, lane, part);
     }
   }
@@ -559,6 +720,8 @@ hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hi
 
 template <class E>
 hipError_t launch_dtype(const Variant& v, const Args& a, dim3 grid, unsigned lds, hipStream_t st) {
+  // only the slot counts the element type may use are instantiated
+  constexpr int kCap4 = max_slots(E::kDtype, 4), kCap16 = max_slots(E::kDtype, 16);
   if (v.nw == 4) {
     switch (v.vpl) {
       case 1: return launch_vpl<E, 1, 4>(v, a, grid, lds, st);
@@ -566,30 +729,24 @@ hipError_t launch_dtype(const Variant& v, const Args& a, dim3 grid, unsigned lds
       case 4: return launch_vpl<E, 4, 4>(v, a, grid, lds, st);
       case 6: return launch_vpl<E, 6, 4>(v, a, grid, lds, st);
       case 8: return launch_vpl<E, 8, 4>(v, a, grid, lds, st);
-      case 10: return launch_vpl<E, 10, 4>(v, a, grid, lds, st);
-      case 12: return launch_vpl<E, 12, 4>(v, a, grid, lds, st);
-      case 16: return launch_vpl<E, 16, 4>(v, a, grid, lds, st);
-      default: return hipErrorInvalidValue;
+      case 10: if constexpr (kCap4 >= 10) return launch_vpl<E, 10, 4>(v, a, grid, lds, st); break;
+      case 12: if constexpr (kCap4 >= 12) return launch_vpl<E, 12, 4>(v, a, grid, lds, st); break;
+      case 16: if constexpr (kCap4 >= 16) return launch_vpl<E, 16, 4>(v, a, grid, lds, st); break;
+      default: break;
     }
+    return hipErrorInvalidValue;
   }
   if (v.nw == 16) {
     switch (v.vpl) {
       case 1: return launch_vpl<E, 1, 16>(v, a, grid, lds, st);
       case 2: return launch_vpl<E, 2, 16>(v, a, grid, lds, st);
       case 4: return launch_vpl<E, 4, 16>(v, a, grid, lds, st);
-      case 8: return launch_vpl<E, 8, 16>(v, a, grid, lds, st);
-      default: return hipErrorInvalidValue;
+      case 8: if constexpr (kCap16 >= 8) return launch_vpl<E, 8, 16>(v, a, grid, lds, st); break;
+      default: break;
     }
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
-
-hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t stream) {
-  if (v.dtype == QKNORM_F32) return launch_dtype<F32>(v, a, grid, lds_bytes, stream);
-  if (v.dtype == QKNORM_BF16) return launch_dtype<BF16>(v, a, grid, lds_bytes, stream);
-  return hipErrorInvalidValue;
-}
-
 }  // namespace qkn

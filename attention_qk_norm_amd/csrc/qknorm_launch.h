@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qknorm.h"
+
 namespace qkn {
 
 enum Mode : int {
@@ -100,9 +102,18 @@ struct Variant {
 constexpr int kVpl4[] = {1, 2, 4, 6, 8, 10, 12, 16};
 constexpr int kVpl16[] = {1, 2, 4, 8};
 
+// Most slots per lane for an element type and workgroup size. An FP8 slot
+// holds its 16-byte vector and two 16-byte weight vectors (bf16 weights), so
+// FP8 stops at 8 slots (4 in 16-wavefront workgroups, whose wavefronts get
+// at most 128 VGPRs) and wider rows take bigger teams instead.
+constexpr int max_slots(int dtype, int nw) {
+  return dtype == QKNORM_FP8_E4M3 ? (nw == 4 ? 8 : 4) : (nw == 4 ? 16 : 8);
+}
+
 // Smallest compiled slot count >= `slots` for `nw` wavefronts per workgroup,
 // or 0 when none is large enough.
-inline int compiled_vpl(int slots, int nw) {
+inline int compiled_vpl(int slots, int nw, int dtype) {
+  if (slots > max_slots(dtype, nw)) return 0;
   if (nw == 4) {
     for (int c : kVpl4)
       if (c >= slots) return c;
@@ -115,7 +126,11 @@ inline int compiled_vpl(int slots, int nw) {
 
 // Enqueue one launch: grid.x workgroups per segment, grid.y segments, with
 // `lds_bytes` of dynamic LDS for staged gamma. Returns hipSuccess or the
-// launch error.
+// launch error. Dispatches on v.dtype to one of the per-type entries below,
+// each built in its own translation unit.
 hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t stream);
+hipError_t launch_f32(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t stream);
+hipError_t launch_bf16(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t stream);
+hipError_t launch_fp8(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t stream);
 
 }  // namespace qkn

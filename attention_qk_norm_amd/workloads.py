@@ -14,8 +14,8 @@ and value spreads are used instead.
 Recipe: numpy `default_rng([workload_id, tensor_id])` with tensor ids
 q=0, k=1, gamma_q=2, gamma_k=3, outlier mask for q=4, for k=5, and the
 per-head weights of the headwise form q=6, k=7. Values are
-drawn in float32; bf16 tensors are then rounded to nearest-even by torch.
-The bf16 values are the problem instance.
+drawn in float32; bf16 and fp8 (OCP e4m3) tensors are then rounded to
+nearest-even by torch. The rounded values are the problem instance.
 """
 from dataclasses import dataclass, field
 from typing import Tuple
@@ -23,13 +23,14 @@ from typing import Tuple
 import numpy as np
 import torch
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 
 TENSOR_Q, TENSOR_K, TENSOR_GQ, TENSOR_GK, MASK_Q, MASK_K, TENSOR_HGQ, TENSOR_HGK = range(8)
 
 # Head width of each workload's model, for the headwise form (the OLMo2
 # shapes use 128-wide heads; the tiny fp32 case cuts its rows into 4 heads).
-HEAD_DIM = {"c1": 64, "c2": 128, "c3": 128, "c4": 128, "c5": 128}
+HEAD_DIM = {"c1": 64, "c2": 128, "c3": 128, "c4": 128, "c5": 128, "c4f8": 128, "c5f8": 128}
 
 
 @dataclass(frozen=True)
@@ -57,13 +58,18 @@ class Workload:
 
     @property
     def elem_bytes(self):
-        return 4 if self.dtype == "f32" else 2
+        return ELEM_BYTES[self.dtype]
+
+    @property
+    def gamma_dtype(self):
+        """The weights' dtype: bf16 for FP8 rows, else the rows' own."""
+        return "bf16" if self.dtype == "fp8" else self.dtype
 
     def algorithmic_bytes(self):
         """Bytes a single fused pass must move: every q and k element read once
         and written once, and each gamma read once."""
         s = self.elem_bytes
-        return 2 * self.T * (self.hq + self.hk) * s + (self.hq + self.hk) * s
+        return 2 * self.T * (self.hq + self.hk) * s + (self.hq + self.hk) * ELEM_BYTES[self.gamma_dtype]
 
 
 WORKLOADS = {
@@ -83,6 +89,14 @@ WORKLOADS = {
     "c5": Workload(5, "large-prefill", 16384, 4096, 4096, "bf16", "laplace",
                    1.0, 0.0, 1.0, 0.5, 1.5, 1e-6, (8, 1), True,
                    "in-place output; 8 slices of 512"),
+    # FP8-E4M3 activations (the review's Fig. 2(b) FP8 runs) on the two
+    # prefill shapes; the weights stay bf16
+    "c4f8": Workload(14, "olmo2-32b-gqa-prefill-fp8", 2048, 5120, 1024, "fp8",
+                     "normal", 1.0, 0.0, 1.0, 0.5, 1.5, 1e-6, (1,), False,
+                     "C4's shape with e4m3 rows"),
+    "c5f8": Workload(15, "large-prefill-fp8", 16384, 4096, 4096, "fp8", "laplace",
+                     1.0, 0.0, 1.0, 0.5, 1.5, 1e-6, (8, 1), True,
+                     "C5's shape with e4m3 rows, in place; 8 slices of 512"),
 }
 
 
@@ -115,7 +129,7 @@ def weights(w, which):
     """Seeded gamma of workload `w` for tensor "q" or "k"."""
     tid, width = (TENSOR_GQ, w.hq) if which == "q" else (TENSOR_GK, w.hk)
     g = np.random.default_rng([w.wid, tid]).uniform(w.gamma_lo, w.gamma_hi, width)
-    return _finish(g.astype(np.float32), w.dtype)
+    return _finish(g.astype(np.float32), w.gamma_dtype)
 
 
 def head_weights(w, which, head_dim):
@@ -123,7 +137,7 @@ def head_weights(w, which, head_dim):
     the tensor) for the headwise form; tensor ids 6 (q) and 7 (k)."""
     tid = TENSOR_HGQ if which == "q" else TENSOR_HGK
     g = np.random.default_rng([w.wid, tid]).uniform(w.gamma_lo, w.gamma_hi, head_dim)
-    return _finish(g.astype(np.float32), w.dtype)
+    return _finish(g.astype(np.float32), w.gamma_dtype)
 
 
 def generate(name):

@@ -28,7 +28,11 @@ sys.path.insert(0, ROOT)
 METRIC = "QK-Norm tokens/sec and achieved HBM GB/s (% of peak) at 1 MI355X"
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 CPU_SHARE = 16         # host cores per GPU on the measurement boxes
-KERNEL_SOURCES = ("attention_qk_norm_amd/csrc/qknorm_kernels.hip",
+KERNEL_SOURCES = ("attention_qk_norm_amd/csrc/qknorm_kernels.h",
+                  "attention_qk_norm_amd/csrc/qknorm_kernels_f32.hip",
+                  "attention_qk_norm_amd/csrc/qknorm_kernels_bf16.hip",
+                  "attention_qk_norm_amd/csrc/qknorm_kernels_fp8.hip",
+                  "attention_qk_norm_amd/csrc/qknorm_launch.cpp",
                   "attention_qk_norm_amd/csrc/qknorm_api.cpp",
                   "attention_qk_norm_amd/csrc/qknorm_launch.h")
 TRAFFIC_FILE = "profiles/qknorm_fwd_{workload}_traffic.json"
@@ -58,7 +62,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
-    p.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"])
+    p.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "c4f8", "c5f8"])
     p.add_argument("--num-slices", type=int, default=None,
                    help="slices of the row statistic (default: the workload's primary count)")
     p.add_argument("--rotate-mib", type=int, default=2048,

@@ -20,13 +20,17 @@
  *    library allocates no device memory and keeps no state between calls.
  *  - Layout: rows are row-major; row t of a tensor starts `stride` ELEMENTS
  *    after row t-1. Widths and strides count elements, not bytes.
- *  - Element types: QKNORM_F32 (IEEE binary32) or QKNORM_BF16 (bfloat16).
- *    gamma has the element type of the rows it scales. Statistics are fp32.
- *    All accumulation is fp32 (review section 5: fp32 accumulation even for
- *    bf16 data). bf16 results are rounded to nearest-even from fp32.
- *  - Vectors: data move in 16-byte vectors (8 bf16 or 4 fp32 elements), so
- *    every pointer must be 16-byte aligned and every width, slice width and
- *    stride a multiple of 8 (bf16) or 4 (fp32) elements.
+ *  - Element types: QKNORM_F32 (IEEE binary32), QKNORM_BF16 (bfloat16) or
+ *    QKNORM_FP8_E4M3 (OCP FP8 E4M3, the activation format of the review's
+ *    Fig. 2(b) FP8 runs). gamma has the element type of the rows it scales,
+ *    except that FP8 rows take bfloat16 weights. Statistics are fp32. All
+ *    accumulation is fp32 (review section 5: fp32 accumulation even for bf16
+ *    or FP8 data). Results are computed in fp32 and rounded to nearest-even
+ *    in the output type; FP8 results saturate at +-448 (NaN stays NaN).
+ *  - Vectors: data move in 16-byte vectors (16 fp8, 8 bf16 or 4 fp32
+ *    elements), so every pointer must be 16-byte aligned and every width,
+ *    slice width and stride a multiple of 16 (fp8), 8 (bf16) or 4 (fp32)
+ *    elements.
  *  - Streams: `stream` is a hipStream_t (NULL = the null stream) on the
  *    context's device, which must also be the calling thread's current
  *    device. Calls only enqueue work; they never synchronise.
@@ -50,10 +54,12 @@
 extern "C" {
 #endif
 
-/* Element type of the rows and of gamma. */
+/* Element type of the rows (and of gamma, except for FP8 rows). */
 typedef enum {
     QKNORM_F32 = 0,
-    QKNORM_BF16 = 1
+    QKNORM_BF16 = 1,
+    QKNORM_FP8_E4M3 = 2   /* OCP FP8 E4M3 rows (no infinities, largest finite
+                             448); gamma is bfloat16 for these rows */
 } qknorm_dtype;
 
 typedef enum {
@@ -151,10 +157,10 @@ int qknorm_forward(qknorm_ctx *ctx, int dtype, int64_t T,
  * of its heads. One kernel launch; each row is read once and written once.
  *
  *   head_dim   columns per head, the same for q and k: one head must be a
- *              power of two of 16-byte vectors, at most 64 of them (bf16:
- *              8, 16, ..., 512 columns; fp32: 4, 8, ..., 256), and each
- *              width a multiple of head_dim
- *   gamma_q, gamma_k  head_dim weights each (element type of the rows)
+ *              power of two of 16-byte vectors, at most 64 of them (fp8:
+ *              16, 32, ..., 1024 columns; bf16: 8, ..., 512; fp32: 4, ...,
+ *              256), and each width a multiple of head_dim
+ *   gamma_q, gamma_k  head_dim weights each (gamma's element type)
  *   dtype, T, q, k, eps, stream: as for qknorm_forward
  * Rows are always streamed (the cached_rows option does not apply).
  * Status, in validation order: QKNORM_ERR_DTYPE, QKNORM_ERR_SHAPE (T < 0),

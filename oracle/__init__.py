@@ -77,14 +77,15 @@ def set_threads(n):
 
 def as_f32(a):
     """Exact float32 view of the values in `a` (numpy array or CPU torch tensor
-    of dtype float32 or bfloat16). Widening bf16 or fp32 to fp32 is exact."""
+    of dtype float32, bfloat16 or float8_e4m3fn). Each widens to fp32
+    exactly."""
     if hasattr(a, "detach"):  # torch tensor
         import torch
         t = a.detach().to("cpu")
-        if t.dtype == torch.bfloat16:
+        if t.dtype in (torch.bfloat16, torch.float8_e4m3fn):
             t = t.to(torch.float32)  # exact widening
         if t.dtype != torch.float32:
-            raise TypeError("oracle takes float32 or bfloat16 data, got %s" % t.dtype)
+            raise TypeError("oracle takes float32, bfloat16 or float8_e4m3fn data, got %s" % t.dtype)
         return np.ascontiguousarray(t.numpy())
     a = np.asarray(a)
     if a.dtype != np.float32:

@@ -112,7 +112,7 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
   const int nseg = hk > 0 ? 2 : 1;
   Plan plans[2];
   int nw = 4;
-  const int st = plan_launch(&ctx, in, nseg, T, plans, &nw);
+  const int st = plan_launch(&ctx, dtype, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) {
     // only a pinned team that cannot hold the row may be refused
     CHECK(forced_wpr != 0, "auto plan refused T=%lld hq=%lld hk=%lld K=%d", (long long)T, (long long)hq,
@@ -127,10 +127,10 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
     Plan pl = plans[i];
     if (masked && !pl.masked) pl = Plan{pl.wpr_log2, pl.wpr_log2, plain_slots(in[i].nvec, pl.wpr_log2), true};
     fill_layout(&seg[i], pl, nw, in[i].nvec, K, T);
-    share_gamma(&seg[i]);
+    share_gamma(&seg[i], dtype);
     slots = seg[i].nslot > slots ? seg[i].nslot : slots;
   }
-  const int vpl = qkn::compiled_vpl(slots, nw);
+  const int vpl = qkn::compiled_vpl(slots, nw, dtype);
   char what[160];
   std::snprintf(what, sizeof what, "T=%lld hq=%lld hk=%lld K=%d wpr=%d dt=%d", (long long)T, (long long)hq,
                 (long long)hk, K, forced_wpr, dtype);
@@ -172,7 +172,7 @@ static void run_headwise(int64_t T, int64_t hq, int64_t hk, int64_t D, int force
   std::snprintf(what, sizeof what, "headwise T=%lld hq=%lld hk=%lld D=%lld wpr=%d dt=%d", (long long)T,
                 (long long)hq, (long long)hk, (long long)D, forced_wpr, dtype);
   CHECK(hv > 0, "%s invalid head", what);
-  if (plan_launch(&ctx, in, nseg, T, plans, &nw) != QKNORM_OK) {
+  if (plan_launch(&ctx, dtype, in, nseg, T, plans, &nw) != QKNORM_OK) {
     CHECK(forced_wpr != 0, "%s auto plan refused", what);
     return;
   }
@@ -183,7 +183,7 @@ static void run_headwise(int64_t T, int64_t hq, int64_t hk, int64_t D, int force
     fill_layout(&seg[i], plans[i], nw, in[i].nvec, 1, T);
     slots = seg[i].nslot > slots ? seg[i].nslot : slots;
   }
-  const int vpl = qkn::compiled_vpl(slots, nw);
+  const int vpl = qkn::compiled_vpl(slots, nw, dtype);
   CHECK(vpl > 0, "%s no compiled variant for %d slots", what, slots);
   if (vpl == 0) return;
   for (int i = 0; i < nseg; ++i) {
@@ -199,7 +199,7 @@ int main() {
   const int64_t rows[] = {1, 3, 64, 256, 2048, 16384};
   const int ks[] = {1, 2, 3, 4, 5, 8, 10, 16, 24, 32, 40, 48, 64};
   const int wprs[] = {0, 1, 2, 4, 8, 16};
-  for (int dtype : {QKNORM_BF16, QKNORM_F32})
+  for (int dtype : {QKNORM_BF16, QKNORM_F32, QKNORM_FP8_E4M3})
     for (int64_t hq : widths)
       for (int K : ks) {
         const int64_t ve = vec_elems(dtype);
@@ -216,7 +216,7 @@ int main() {
             }
           }
       }
-  for (int dtype : {QKNORM_BF16, QKNORM_F32})
+  for (int dtype : {QKNORM_BF16, QKNORM_F32, QKNORM_FP8_E4M3})
     for (int64_t hq : widths)
       for (int64_t D = 1; D <= hq; D *= 2) {
         if (hq > qknorm_max_width(dtype) || head_vectors(D, dtype) == 0 || hq % D) continue;

@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_binding_constants_match_header():
-    for pyname, cname in (("F32", "QKNORM_F32"), ("BF16", "QKNORM_BF16"), ("OK", "QKNORM_OK"),
+    for pyname, cname in (("F32", "QKNORM_F32"), ("BF16", "QKNORM_BF16"), ("FP8_E4M3", "QKNORM_FP8_E4M3"),
+                          ("OK", "QKNORM_OK"),
                           ("ERR_NULL", "QKNORM_ERR_NULL"), ("ERR_SHAPE", "QKNORM_ERR_SHAPE"),
                           ("ERR_SLICES", "QKNORM_ERR_SLICES"), ("ERR_ALIGN", "QKNORM_ERR_ALIGN"),
                           ("ERR_DTYPE", "QKNORM_ERR_DTYPE"), ("ERR_EPS", "QKNORM_ERR_EPS"),
@@ -59,6 +60,7 @@ def test_status_strings():
 def test_max_width():
     assert qk.max_width(qk.BF16) == 65536
     assert qk.max_width(qk.F32) == 32768
+    assert qk.max_width(qk.FP8_E4M3) == 65536
     assert qk.max_width(7) == 0
 
 
@@ -86,7 +88,7 @@ def test_forward_empty_is_ok(L):
 def test_forward_rejects(L):
     R = qk.Rows
     cases = [
-        (dict(dtype=2), qk.ERR_DTYPE),
+        (dict(dtype=3), qk.ERR_DTYPE),
         (dict(T=-1), qk.ERR_SHAPE),
         (dict(T=1 << 31), qk.ERR_SHAPE),
         (dict(q=R(0, A + 8 * MB, 4096, 4096, 4096)), qk.ERR_NULL),
@@ -138,6 +140,29 @@ def test_forward_slice_width_must_be_whole_vectors(L):
     assert _fwd(L, dtype=qk.F32, q=q, k=None, K=8) == qk.ERR_SLICES
 
 
+def test_fp8_rows(L):
+    """FP8 rows move 16 elements per vector; their weights are bf16, so a
+    weight vector is twice the row's bytes."""
+    R = qk.Rows
+    q, k = R(A, A + 8 * MB, 4096, 4096, 4096), R(A + 16 * MB, A + 24 * MB, 1024, 1024, 1024)
+    assert _fwd(L, dtype=qk.FP8_E4M3, q=q, k=k, K=8) == qk.ERR_CONTEXT
+    # 4096 / 512 = 8 fp8 elements: half a vector
+    assert _fwd(L, dtype=qk.FP8_E4M3, q=q, k=k, K=512) == qk.ERR_SLICES
+    assert _fwd(L, dtype=qk.FP8_E4M3, q=R(A, A + 8 * MB, 4104, 4104, 4104), k=k) == qk.ERR_ALIGN
+    assert _fwd(L, dtype=qk.FP8_E4M3, q=R(A, A + 8 * MB, 65536, 65536, 65536), k=None) == qk.ERR_CONTEXT
+    assert _fwd(L, dtype=qk.FP8_E4M3, q=R(A, A + 8 * MB, 65536 + 16, 65552, 65552), k=None) == qk.ERR_SHAPE
+    # the query output placed right after 4096 bf16 weights (8 KiB) is clear
+    # of them; 4 KiB after them (the fp8 row length) is not
+    q2 = R(A, A + 60 * MB + 8192, 4096, 4096, 4096)
+    assert _fwd(L, dtype=qk.FP8_E4M3, q=q2, k=None) == qk.ERR_CONTEXT
+    q3 = R(A, A + 60 * MB + 4096, 4096, 4096, 4096)
+    assert _fwd(L, dtype=qk.FP8_E4M3, q=q3, k=None) == qk.ERR_ALIAS
+    # headwise: heads are a power of two of 16-byte vectors, 16 ... 1024 fp8 columns
+    for D, want in ((16, qk.ERR_CONTEXT), (128, qk.ERR_CONTEXT), (1024, qk.ERR_CONTEXT), (8, qk.ERR_SLICES),
+                    (2048, qk.ERR_SLICES), (48, qk.ERR_SLICES)):
+        assert _head(L, dtype=qk.FP8_E4M3, D=D) == want, D
+
+
 def test_forward_in_place_and_packed_qkv_are_accepted(L):
     R = qk.Rows
     # in place, same stride
@@ -178,7 +203,7 @@ def test_headwise_validation(L):
     assert _head(L, D=512) == qk.ERR_CONTEXT
     assert _head(L, D=256, k=R(A + 16 * MB, A + 24 * MB, 1152, 1152, 1152)) == qk.ERR_SLICES
     cases = [
-        (dict(dtype=2), qk.ERR_DTYPE),
+        (dict(dtype=3), qk.ERR_DTYPE),
         (dict(T=-1), qk.ERR_SHAPE),
         (dict(gq=None), qk.ERR_NULL),
         (dict(q=R(A, A + 8 * MB, 4096, 4088, 4096)), qk.ERR_SHAPE),
