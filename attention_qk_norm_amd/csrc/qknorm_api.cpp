@@ -239,9 +239,11 @@ struct SegIn {
 //    one workgroup per row, until there are 2 wavefronts per SIMD, so each
 //    row's loads are spread over more wavefronts and finish sooner;
 //  - 8 or more rows per SIMD (long prefill launches, several rounds of
-//    wavefronts per SIMD): two wavefronts share each row, so each holds half
-//    a row and its writes start sooner after its reads (3% faster at
-//    16384 x 4096, no slower on the grouped-query shape);
+//    wavefronts per SIMD): a row that would take a wavefront 8 or more slots
+//    is shared by two wavefronts, so each holds half a row and its writes
+//    start sooner after its reads (bf16 16384 x 4096, 8 slots: 3% faster);
+//    with fewer slots one wavefront per row stays faster (FP8 16384 x 4096,
+//    4 slots: 47.7 us against 50.7 us with two);
 //  - in between, every row's loads are issued in the first round, and one
 //    wavefront per row is fastest.
 int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int64_t T, Plan* plans, int* nw) {
@@ -265,7 +267,7 @@ int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int
     const int64_t simds = int64_t{4} * ctx->num_cus;
     if (T * nseg >= 8 * simds) {
       for (int i = 0; i < nseg; ++i) {
-        if (plans[i].wpr_log2 != 0) continue;
+        if (plans[i].wpr_log2 != 0 || plans[i].slots < 8) continue;
         const Plan p = plans[i].masked ? Plan{1, 1, plain_slots(in[i].nvec, 1), true}
                                        : seg_plan(in[i].nvec / in[i].K, in[i].K, 1);
         if (p.slots <= cap4) plans[i] = p;
@@ -316,6 +318,13 @@ void fill_layout(qkn::Seg* s, const Plan& p, int nw, int64_t nvec, int K, int64_
     s->slot_lim[j] = 0;
   }
   if (p.masked) {
+    // slices of 2^g <= 32 vectors tile each wavefront's 64 lanes exactly
+    s->grouped = 0;
+    s->group_log2 = 0;
+    if (slice_vec <= 32 && (slice_vec & (slice_vec - 1)) == 0) {
+      s->grouped = 1;
+      while ((int64_t{1} << s->group_log2) < slice_vec) ++s->group_log2;
+    }
     s->nslot = static_cast<int32_t>(ceil_div(nvec, ns));
     for (int j = 0; j < s->nslot; ++j) {
       s->slot_base[j] = static_cast<int32_t>(j * ns);

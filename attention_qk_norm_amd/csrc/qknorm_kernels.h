@@ -173,15 +173,17 @@ struct FP8 {
   static __device__ __forceinline__ G gamma_lds(const u32x4* lds, uint32_t v) {
     return G{lds[2u * v], lds[2u * v + 1u]};
   }
+  // Squares: each pair widens exactly to bf16 (the scaled conversion with
+  // scale 1; e4m3 values, subnormals included, are bf16 values) and one
+  // bf16 dot product adds both squares to the fp32 accumulator: two
+  // instructions per pair instead of a widening to fp32 and two FMAs.
   static __device__ __forceinline__ float sumsq(u32x4 d, float acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x2 a = fp8_pair(d[i], false);
-      const f32x2 b = fp8_pair(d[i], true);
-      acc = __builtin_fmaf(a.x, a.x, acc);
-      acc = __builtin_fmaf(a.y, a.y, acc);
-      acc = __builtin_fmaf(b.x, b.x, acc);
-      acc = __builtin_fmaf(b.y, b.y, acc);
+      const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[i], 1.0f, false);
+      const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[i], 1.0f, true);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(a, a, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(b, b, acc, false);
     }
     return acc;
   }
@@ -281,7 +283,8 @@ struct Hot {
   const float* stats_in;
   float* stats_out;
   int64_t x_stride, y_stride, T;
-  int rows_per_wg, nwg, nslot, wpr_log2, sub_log2, lds_gamma, lay_k, comb_k, slice_vec, head_log2, emit_rinv;
+  int rows_per_wg, nwg, nslot, wpr_log2, sub_log2, lds_gamma, lay_k, comb_k, slice_vec, head_log2, emit_rinv,
+      grouped, group_log2;
   uint32_t row_bytes, flush_mask;
   float inv_slice_vec, h, inv_h, eps;
 
@@ -290,6 +293,7 @@ struct Hot {
         x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
         nslot(s.nslot), wpr_log2(s.wpr_log2), sub_log2(s.sub_log2), lds_gamma(s.lds_gamma),
         lay_k(s.lay_k), comb_k(s.comb_k), slice_vec(s.slice_vec), head_log2(s.head_log2), emit_rinv(s.emit_rinv),
+        grouped(s.grouped), group_log2(s.group_log2),
         row_bytes(s.row_bytes), flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h),
         inv_h(s.inv_h), eps(a.eps) {}
 };
@@ -305,6 +309,12 @@ struct Tables {
       lim[j] = s.slot_lim[j];
       base[j] = s.slot_base[j];
     }
+    // Pin every entry here, before the dispatch on the slot count: left to
+    // itself the compiler sinks the loads of entries only the wider bodies
+    // use past that branch, which costs each launch a second round trip to
+    // memory before its first row load. The empty asm emits nothing.
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) asm volatile("" : "+s"(lim[j]), "+s"(base[j]));
   }
 };
 
@@ -358,118 +368,6 @@ __device__ __forceinline__ void load_gamma(typename E::G (&g)[VPL], const Hot& s
   for (int j = 0; j < VPL; ++j) g[j] = E::load_gamma(r, L.off[j]);
 }
 
-// The row statistic S = sum over slices (ascending) of each slice's sum of
-// squares. Teams of several wavefronts add their partials through `part`
-// (one barrier); every lane of the team returns the same S.
-template <class E, int VPL, bool MASKED>
-__device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, const Layout<VPL>& L,
-                                          int wave, int lane, float* part) {
-  float S = 0.f;
-  if constexpr (!MASKED) {
-    // slots are grouped by slice; a set bit in flush_mask closes a slice
-    float p = 0.f;
-    int slice = 0;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      p = E::sumsq(d[j], p);
-      if ((s.flush_mask >> j) & 1u) {
-        const float P = wave_sum(p);
-        p = 0.f;
-        if (L.wpr == 1)
-          S += P;
-        else if (lane == 0)
-          part[wave * kWave + slice] = P;
-        ++slice;
-      }
-    }
-  } else {
-    // plain strided slots; each vector's squares join the partial of the
-    // slice its index falls in
-    float q[VPL];
-    int sid[VPL];
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      q[j] = E::sumsq(d[j], 0.f);
-      sid[j] = slice_of(L.base[j], s.slice_vec, s.inv_slice_vec);
-    }
-    for (int k = 0; k < s.lay_k; ++k) {
-      float p = 0.f;
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) p += (sid[j] == k) ? q[j] : 0.f;
-      const float P = wave_sum(p);
-      if (L.wpr == 1)
-        S += P;
-      else if (lane == 0)
-        part[wave * kWave + k] = P;
-    }
-  }
-  if (L.wpr > 1) {
-    // slice k's partial comes from the wavefronts of sub-team k % nsub, at
-    // index k / nsub of their partial lists; slices are added in ascending k
-    // lane k gathers slice k's partials (one LDS round trip for all lanes),
-    // then the slices are added in ascending k
-    __syncthreads();
-    const int w0 = L.team << L.wpr_log2;
-    const int sub_log2 = MASKED ? L.wpr_log2 : s.sub_log2;
-    const int nsub_log2 = L.wpr_log2 - sub_log2;
-    float Pk = 0.f;
-    if (lane < s.lay_k) {
-      const int w1 = w0 + ((lane & ((1 << nsub_log2) - 1)) << sub_log2);
-      const int i = lane >> nsub_log2;
-      for (int w = 0; w < (1 << sub_log2); ++w) Pk += part[(w1 + w) * kWave + i];
-    }
-    for (int k = 0; k < s.lay_k; ++k) S += lane_value(Pk, k);
-    __syncthreads();  // `part` is free again
-  }
-  return S;
-}
-
-// The inverse RMS of a row (review Eq. 6): the fused forward and the
-// statistic-only output use this same expression, so they agree bit for bit.
-__device__ __forceinline__ float inv_rms(float S, float h, float eps) {
-  return 1.0f / __builtin_sqrtf(S / h + eps);
-}
-
-// BOUNDED: S covers every element scaled here (not so for partials handed in
-// by a caller), so |x r| <= sqrt(h) and the weights alone decide whether a
-// result can saturate.
-template <class E, int VPL, bool NT, bool BOUNDED>
-__device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], float S,
-                                            float h, float eps, __amdgpu_buffer_rsrc_t yr,
-                                            const Layout<VPL>& L) {
-  const float r = inv_rms(S, h, eps);
-  if (!BOUNDED || E::may_saturate(g, h)) {
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::template scale<true>(d[j], g[j], r));
-  } else {
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::template scale<false>(d[j], g[j], r));
-  }
-}
-
-// Finish one row whose data (and weights) are in registers: statistic (or
-// the precomputed partials), then scale and store, or publish the statistic.
-template <class E, int VPL, int MODE, bool MASKED, bool NT>
-__device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], const Hot& s,
-                                           const Layout<VPL>& L, int64_t row, bool live, int wave,
-                                           int lane, float* part) {
-  float S = 0.f;
-  if constexpr (MODE == MODE_APPLY) {
-    // lane k fetches partial k; then they are added in ascending k
-    float pk = 0.f;
-    if (live && lane < s.comb_k) pk = s.stats_in[static_cast<int64_t>(lane) * s.T + row];
-    for (int k = 0; k < s.comb_k; ++k) S += lane_value(pk, k);
-  } else {
-    S = row_stat<E, VPL, MASKED>(d, s, L, wave, lane, part);
-  }
-  if constexpr (MODE == MODE_STATS) {
-    if (live && L.tl == 0) s.stats_out[row] = s.emit_rinv ? inv_rms(S, s.h, s.eps) : S;
-  } else {
-    scale_store<E, VPL, NT, MODE != MODE_APPLY>(d, g, S, s.h, s.eps,
-                                                row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
-  }
-}
-
 // Headwise (review, "Layerwise vs. headwise QK-Norm"): sums over aligned
 // groups of 2^hl lanes (hl <= 6), one group per head, every lane of a group
 // receiving the same value. Within a row of 16 lanes each butterfly step
@@ -505,6 +403,161 @@ __device__ __forceinline__ void head_sums(float (&q)[V], int hl, int lane) {
 #pragma unroll
     for (int j = 0; j < V; ++j)
       q[j] = (lane_value(q[j], 0) + lane_value(q[j], 16)) + (lane_value(q[j], 32) + lane_value(q[j], 48));
+  }
+}
+
+// Grouped layout: slice k of the row is the aligned group of 2^gl lanes
+// holding vectors k 2^gl ... (k+1) 2^gl - 1 in one slot of one wavefront:
+// slot j, wavefront w of the team, group g give slice
+// k = (j wpr + w) 2^(6-gl) + g. Group sums come from the same butterfly as
+// the headwise form, read from each group's first lane (groups of 32 add
+// two 16-lane row sums); then the slices are added in ascending k, through
+// LDS when the team has several wavefronts.
+template <class E, int VPL>
+__device__ __forceinline__ float grouped_stat(const u32x4 (&d)[VPL], const Hot& s, const Layout<VPL>& L,
+                                              int wave, int lane, float* part, bool reuse) {
+  float q[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) q[j] = E::sumsq(d[j], 0.f);
+  const int gl = s.group_log2;
+  head_sums<VPL>(q, gl < 4 ? gl : 4, lane);  // groups of up to 16 lanes
+  const int sv = 1 << gl;
+  const int ng = 64 >> gl;  // groups (slices) per wavefront slot
+  const int wi = wave & (L.wpr - 1);
+  float S = 0.f;
+  const int w0 = L.team << L.wpr_log2;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int k0 = ((j << L.wpr_log2) + wi) * ng;  // first slice of this wavefront's slot j
+    for (int g = 0; g < ng; ++g) {
+      const float P = gl == 5 ? lane_value(q[j], g * 32) + lane_value(q[j], g * 32 + 16)
+                              : lane_value(q[j], g * sv);
+      if (L.wpr == 1)
+        S += P;  // slot-major, group-minor: ascending k
+      else if (lane == 0 && k0 + g < s.lay_k)
+        part[w0 * kWave + k0 + g] = P;
+    }
+  }
+  if (L.wpr > 1) {
+    __syncthreads();
+    const float Pk = lane < s.lay_k ? part[w0 * kWave + lane] : 0.f;
+    for (int k = 0; k < s.lay_k; ++k) S += lane_value(Pk, k);
+    if (reuse) __syncthreads();  // `part` is free again
+  }
+  return S;
+}
+
+// The row statistic S = sum over slices (ascending) of each slice's sum of
+// squares. Teams of several wavefronts add their partials through `part`
+// (one barrier, and a second one only when `reuse`: the workgroup goes on to
+// combine another row there; uniform over the workgroup); every lane of the
+// team returns the same S.
+template <class E, int VPL, bool MASKED>
+__device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, const Layout<VPL>& L,
+                                          int wave, int lane, float* part, bool reuse) {
+  float S = 0.f;
+  if constexpr (!MASKED) {
+    // slots are grouped by slice; a set bit in flush_mask closes a slice
+    float p = 0.f;
+    int slice = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      p = E::sumsq(d[j], p);
+      if ((s.flush_mask >> j) & 1u) {
+        const float P = wave_sum(p);
+        p = 0.f;
+        if (L.wpr == 1)
+          S += P;
+        else if (lane == 0)
+          part[wave * kWave + slice] = P;
+        ++slice;
+      }
+    }
+  } else {
+    if (s.grouped) return grouped_stat<E, VPL>(d, s, L, wave, lane, part, reuse);
+    // plain strided slots; each vector's squares join the partial of the
+    // slice its index falls in
+    float q[VPL];
+    int sid[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      q[j] = E::sumsq(d[j], 0.f);
+      sid[j] = slice_of(L.base[j], s.slice_vec, s.inv_slice_vec);
+    }
+    for (int k = 0; k < s.lay_k; ++k) {
+      float p = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) p += (sid[j] == k) ? q[j] : 0.f;
+      const float P = wave_sum(p);
+      if (L.wpr == 1)
+        S += P;
+      else if (lane == 0)
+        part[wave * kWave + k] = P;
+    }
+  }
+  if (L.wpr > 1) {
+    // slice k's partials come from the wavefronts of sub-team k % nsub, at
+    // index k / nsub of their partial lists; lane k gathers them (one LDS
+    // round trip for all lanes), then the slices are added in ascending k
+    __syncthreads();
+    const int w0 = L.team << L.wpr_log2;
+    const int sub_log2 = MASKED ? L.wpr_log2 : s.sub_log2;
+    const int nsub_log2 = L.wpr_log2 - sub_log2;
+    float Pk = 0.f;
+    if (lane < s.lay_k) {
+      const int w1 = w0 + ((lane & ((1 << nsub_log2) - 1)) << sub_log2);
+      const int i = lane >> nsub_log2;
+      for (int w = 0; w < (1 << sub_log2); ++w) Pk += part[(w1 + w) * kWave + i];
+    }
+    for (int k = 0; k < s.lay_k; ++k) S += lane_value(Pk, k);
+    if (reuse) __syncthreads();  // `part` is free again
+  }
+  return S;
+}
+
+// The inverse RMS of a row (review Eq. 6): the fused forward and the
+// statistic-only output use this same expression, so they agree bit for bit.
+__device__ __forceinline__ float inv_rms(float S, float h, float eps) {
+  return 1.0f / __builtin_sqrtf(S / h + eps);
+}
+
+// BOUNDED: S covers every element scaled here (not so for partials handed in
+// by a caller), so |x r| <= sqrt(h) and the weights alone decide whether a
+// result can saturate.
+template <class E, int VPL, bool NT, bool BOUNDED>
+__device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], float S,
+                                            float h, float eps, __amdgpu_buffer_rsrc_t yr,
+                                            const Layout<VPL>& L) {
+  const float r = inv_rms(S, h, eps);
+  if (!BOUNDED || E::may_saturate(g, h)) {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::template scale<true>(d[j], g[j], r));
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::template scale<false>(d[j], g[j], r));
+  }
+}
+
+// Finish one row whose data (and weights) are in registers: statistic (or
+// the precomputed partials), then scale and store, or publish the statistic.
+template <class E, int VPL, int MODE, bool MASKED, bool NT>
+__device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], const Hot& s,
+                                           const Layout<VPL>& L, int64_t row, bool live, int wave,
+                                           int lane, float* part, bool reuse) {
+  float S = 0.f;
+  if constexpr (MODE == MODE_APPLY) {
+    // lane k fetches partial k; then they are added in ascending k
+    float pk = 0.f;
+    if (live && lane < s.comb_k) pk = s.stats_in[static_cast<int64_t>(lane) * s.T + row];
+    for (int k = 0; k < s.comb_k; ++k) S += lane_value(pk, k);
+  } else {
+    S = row_stat<E, VPL, MASKED>(d, s, L, wave, lane, part, reuse);
+  }
+  if constexpr (MODE == MODE_STATS) {
+    if (live && L.tl == 0) s.stats_out[row] = s.emit_rinv ? inv_rms(S, s.h, s.eps) : S;
+  } else {
+    scale_store<E, VPL, NT, MODE != MODE_APPLY>(d, g, S, s.h, s.eps,
+                                                row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
   }
 }
 
@@ -588,13 +641,13 @@ __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L
     const int g1 = g0 + G;
     const int64_t rb = static_cast<int64_t>(g1) * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(B, row_rsrc<E>(s.x, s.x_stride, rb, g1 < s.nwg && rb < s.T, s.row_bytes), L);
-    float S = row_stat<E, VPL, MASKED>(A, s, L, wave, lane, part);
+    float S = row_stat<E, VPL, MASKED>(A, s, L, wave, lane, part, true);
     scale_store<E, VPL, NT, true>(A, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, ra, ra < s.T, s.row_bytes), L);
     if (g1 >= s.nwg) break;
     const int g2 = g1 + G;
     ra = static_cast<int64_t>(g2) * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(A, row_rsrc<E>(s.x, s.x_stride, ra, g2 < s.nwg && ra < s.T, s.row_bytes), L);
-    S = row_stat<E, VPL, MASKED>(B, s, L, wave, lane, part);
+    S = row_stat<E, VPL, MASKED>(B, s, L, wave, lane, part, true);
     scale_store<E, VPL, NT, true>(B, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, rb, rb < s.T, s.row_bytes), L);
     if (g2 >= s.nwg) break;
     g0 = g2;
@@ -638,7 +691,8 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
       else
         load_gamma<E, V>(g, s, L);
     }
-    row_finish<E, V, MODE, MASKED, NT>(d, g, s, L, row, live, wave, lane, part);
+    row_finish<E, V, MODE, MASKED, NT>(d, g, s, L, row, live, wave, lane, part,
+                                       gi + static_cast<int>(gridDim.x) < s.nwg);
     // Only grids capped at the hardware limit get here. Reloading gamma each
     // time keeps the first row's registers free of this loop (holding them
     // across it costs about 40 VGPRs).
@@ -649,7 +703,8 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
       typename E::G g2[V];
       load_row<E, V, NT>(d2, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
       if constexpr (MODE != MODE_STATS) load_gamma<E, V>(g2, s, L);
-      row_finish<E, V, MODE, MASKED, NT>(d2, g2, s, L, row, live, wave, lane, part);
+      row_finish<E, V, MODE, MASKED, NT>(d2, g2, s, L, row, live, wave, lane, part,
+                                         gi + static_cast<int>(gridDim.x) < s.nwg);
     }
   }
 }

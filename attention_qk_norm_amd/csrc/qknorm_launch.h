@@ -15,6 +15,9 @@
 // When that would need too many slots (many slices narrower than the team),
 // the kernel falls back to the "masked" layout: plain strided vectors, and a
 // per-lane slice index selects which partial each vector's squares join.
+// When a slice is a power of two of at most 32 vectors, the strided layout
+// puts each slice in one aligned group of lanes of one slot ("grouped"), and
+// the partials come from group sums instead of per-lane masks.
 //
 // Headwise rows use the one-slice (strided) layout. A head is a power of two
 // of at most 64 vectors, so each head sits in one slot of one aligned group
@@ -66,6 +69,8 @@ struct Seg {
   int32_t head_log2;      // HEAD: log2 of the 16-byte vectors per head (0 ... 6)
   float inv_h;            // HEAD: 1 / head width (a power of two, so exact)
   int32_t emit_rinv;      // STATS: write 1 / sqrt(S / h + eps) instead of S
+  int32_t grouped;        // masked layout whose slices are aligned lane groups of
+  int32_t group_log2;     //   2^group_log2 (<= 32) vectors: group sums, no masks
   int32_t slot_base[kMaxSlots];
   int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
 };

@@ -105,6 +105,8 @@ static void check_seg(const qkn::Seg& s, int nw, int vpl, int64_t nvec, int K, b
   }
 }
 
+static void check_heads(const qkn::Seg& s, int hv, const char* what);
+
 static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr, int dtype) {
   qknorm_ctx ctx{0, 256, qknorm_options{forced_wpr, 0, 0}};
   const int64_t ve = vec_elems(dtype);
@@ -136,7 +138,14 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
                 (long long)hk, K, forced_wpr, dtype);
   CHECK(vpl > 0, "%s no compiled variant for %d slots", what, slots);
   if (vpl == 0) return;
-  for (int i = 0; i < nseg; ++i) check_seg(seg[i], nw, vpl, in[i].nvec, K, masked, what);
+  for (int i = 0; i < nseg; ++i) {
+    check_seg(seg[i], nw, vpl, in[i].nvec, K, masked, what);
+    // grouped: every slice is one aligned lane group of one slot, in order
+    if (masked && seg[i].grouped) {
+      CHECK((int64_t{1} << seg[i].group_log2) * K == in[i].nvec, "%s group size", what);
+      check_heads(seg[i], 1 << seg[i].group_log2, what);
+    }
+  }
 }
 
 // Headwise: each aligned group of hv lanes of one wavefront holds, in each

@@ -111,28 +111,34 @@ def test_four_element_closed_form_on_gpu():
     assert_parity(y, np.array([[0.8, 0.8, -1.6, 1.6]]), torch.float32, "gamma")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def bits(t):
+    return t.cpu().contiguous().view(torch.uint8)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 def test_exact_sums_bitwise_across_slicings(dtype):
-    """On n/16 inputs every partial is exact in fp32, so the statistic is the
-    same whatever the slicing: K-slice outputs are bitwise those of K = 1, and
-    the split path's partials equal the exact integer sums."""
+    """On n/16 inputs (exact in fp32, bf16 and e4m3) every partial is exact in
+    fp32, so the statistic is the same whatever the slicing: K-slice outputs
+    are bitwise those of K = 1, and the split path's partials equal the exact
+    integer sums (which also pins each type's decoding of the squares)."""
     T, H = 37, 4096
     x = workloads.exact_sum_rows(T, H, dtype, 71)
     k = workloads.exact_sum_rows(T, 1024, dtype, 72)
-    gq = workloads.random_weights(H, dtype, 73)
-    gk = workloads.random_weights(1024, dtype, 74)
+    gdt = "bf16" if dtype == "fp8" else dtype
+    gq = workloads.random_weights(H, gdt, 73)
+    gk = workloads.random_weights(1024, gdt, 74)
     n = np.rint(host64(x) * 16).astype(np.int64)
     base = None
     for K in (1, 2, 4, 8, 16, 32, 64):
         say("exact sums", dtype, "K=%d" % K)
         yq, yk = run_forward(x, k, gq, gk, 1e-6, K)
         if base is None:
-            base = (yq.cpu(), yk.cpu())
+            base = (bits(yq), bits(yk))
             ref, _ = oracle.forward(x, gq, 1e-6, 1)
             assert_parity(yq, ref, workloads.DTYPES[dtype], "exact-sum forward")
         else:
-            assert torch.equal(yq.cpu(), base[0]), K
-            assert torch.equal(yk.cpu(), base[1]), K
+            assert torch.equal(bits(yq), base[0]), K
+            assert torch.equal(bits(yk), base[1]), K
         w = H // K
         xd = gpu(x)
         stats = torch.zeros((K, T), dtype=torch.float32, device=DEV)
@@ -189,7 +195,11 @@ RAGGED = [
     ("bf16", 5, 1000, 200, 5),       # ragged last slot, slices of 200 / 40
     ("bf16", 63, 1032, 520, 1),
     ("bf16", 65, 5120, 1024, 4),     # C3/C4 widths, odd T
-    ("bf16", 7, 4096, 4096, 64),     # 64 slices of 64: masked layout
+    ("bf16", 7, 4096, 4096, 64),     # 64 slices of 8 vectors: grouped layout
+    ("bf16", 7, 1536, 1536, 64),     # slices of 3 vectors: masked layout
+    ("bf16", 11, 2048, 512, 32),     # groups of 8 and 2 vectors
+    ("bf16", 5000, 1024, 1024, 8),   # groups of 16, two wavefronts per row (LDS combine)
+    ("f32", 9, 4096, 256, 64),       # groups of 16 and of 1 vector
     ("bf16", 9, 12288, 1536, 3),
     ("bf16", 4, 16384, 16384, 8),    # wider than one wavefront's 16 slots
     ("bf16", 3, 65536, 8, 1),        # widest accepted row, with a tiny key row
@@ -200,7 +210,8 @@ RAGGED = [
     ("f32", 17, 4096, 1024, 2),
     ("f32", 3, 8192, 8192, 8),
     ("f32", 2, 32768, 4, 1),         # widest fp32 row
-    ("f32", 5, 1536, 1536, 48),      # 48 slices of 32: masked layout
+    ("f32", 5, 1536, 1536, 48),      # 48 slices of 8 vectors: grouped layout
+    ("f32", 5, 1920, 1920, 40),      # slices of 12 vectors: masked layout
 ]
 
 
