@@ -1,0 +1,94 @@
+"""The library under a serving loop's conditions: calls captured in a HIP
+graph and replayed, and calls on several streams at once. The library keeps
+no state between calls and allocates nothing, so both must reproduce the
+eager results bit for bit."""
+import pytest
+import torch
+
+import attention_qk_norm_amd as qk
+from attention_qk_norm_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def bits(t):
+    return t.cpu().contiguous().view(torch.uint8)
+
+
+def test_graph_capture_and_replay():
+    """Fused forward (K = 4), headwise and inverse RMS captured in one graph;
+    each replay, with unrelated eager work and a synchronisation in between,
+    matches the eager call on fresh inputs copied into the captured buffers."""
+    T, Hq, Hk = 96, 4096, 1024
+    q = torch.empty((T, Hq), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty((T, Hk), dtype=torch.bfloat16, device=DEV)
+    gq = workloads.random_weights(Hq, "bf16", 1).to(DEV)
+    gk = workloads.random_weights(Hk, "bf16", 2).to(DEV)
+    hg = workloads.random_weights(128, "bf16", 3).to(DEV)
+    yq, yk = torch.empty_like(q), torch.empty_like(k)
+    hq, hk = torch.empty_like(q), torch.empty_like(k)
+    rq = torch.empty(T, device=DEV)
+    rk = torch.empty(T, device=DEV)
+
+    def calls(stream):
+        qk.forward(q, k, gq, gk, eps=1e-6, num_slices=4, out_q=yq, out_k=yk, stream=stream)
+        qk.forward_headwise(q, k, hg, hg, 128, eps=1e-6, out_q=hq, out_k=hk, stream=stream)
+        qk.inv_rms(q, k, eps=1e-6, num_slices=4, out_q=rq, out_k=rk, stream=stream)
+
+    s = torch.cuda.Stream()
+    q.copy_(workloads.random_rows(T, Hq, "bf16", 10).to(DEV))
+    k.copy_(workloads.random_rows(T, Hk, "bf16", 11).to(DEV))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):  # warm the stream, as capture requires
+        calls(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("capture")
+    with torch.cuda.graph(g, stream=s):
+        calls(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        q.copy_(workloads.random_rows(T, Hq, "bf16", 100 + rep).to(DEV))
+        k.copy_(workloads.random_rows(T, Hk, "bf16", 200 + rep).to(DEV))
+        torch.cuda.synchronize()
+        say("replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [bits(t) for t in (yq, yk, hq, hk, rq, rk)]
+        junk = torch.randn(1 << 20, device=DEV).sum()  # unrelated eager work between replays
+        calls(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        want = [bits(t) for t in (yq, yk, hq, hk, rq, rk)]
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), rep
+        del junk
+
+
+def test_concurrent_streams():
+    """Independent batches on four streams at once give the results each
+    gives alone."""
+    T, H = 300, 4096
+    xs = [workloads.random_rows(T, H, "bf16", 30 + i).to(DEV) for i in range(4)]
+    g = workloads.random_weights(H, "bf16", 40).to(DEV)
+    alone = []
+    for x in xs:
+        y, _ = qk.forward(x, None, g, None, eps=1e-6, num_slices=8)
+        torch.cuda.synchronize()
+        alone.append(bits(y))
+    streams = [torch.cuda.Stream() for _ in xs]
+    outs = [torch.empty_like(x) for x in xs]
+    torch.cuda.synchronize()
+    say("four streams")
+    for _ in range(3):
+        for x, o, st in zip(xs, outs, streams):
+            with torch.cuda.stream(st):
+                qk.forward(x, None, g, None, eps=1e-6, num_slices=8, out_q=o, stream=st)
+        torch.cuda.synchronize()
+        for o, a in zip(outs, alone):
+            assert torch.equal(bits(o), a)
