@@ -22,6 +22,10 @@
 // MODE_APPLY skips step 2 and combines precomputed partials instead (Phase
 // B's scalar sum, then Phase C). MODE_HEAD is the headwise form.
 //
+// Element types are traits structs (F32, BF16, FP8): vector width, squares,
+// scaling and the weights' type and layout. FP8 rows (OCP E4M3, the review's
+// Fig. 2(b) FP8 runs) take bf16 weights.
+//
 // No matrix cores: the work is a reduction and an elementwise scale, bound by
 // HBM bandwidth.
 #pragma once

@@ -242,7 +242,43 @@ def secondary(torch, qk, workloads, w, args, K, sets, gq, gk, ctx, stream, dev, 
     if max(w.slices) > 1:
         extra.update(split_path(torch, qk, w, sets, gq, gk, ctx, stream, timed, max(w.slices), args))
 
+    # the same shape with FP8-E4M3 rows (bf16 weights), when one exists
+    f8 = args.workload + "f8"
+    if f8 in workloads.WORKLOADS:
+        extra["fp8"] = fp8_figures(torch, qk, workloads, f8, args, ctx, stream, dev, timed)
     return extra
+
+
+def fp8_figures(torch, qk, workloads, name, args, ctx, stream, dev, timed):
+    """The fused forward on the FP8 version of the workload, rotated over
+    buffer sets like the main figure, for each of its slice counts."""
+    d = workloads.generate(name)
+    w = d["w"]
+    nb = w.T * (w.hq + w.hk) * w.elem_bytes * (1 if w.in_place else 2)
+    nsets = max(2, math.ceil(args.rotate_mib * 2**20 / nb))
+    q0, k0 = d["q"].to(dev), d["k"].to(dev)
+    gq, gk = d["gamma_q"].to(dev), d["gamma_k"].to(dev)
+    sets = []
+    for _ in range(nsets):
+        q, k = q0.clone(), k0.clone()
+        sets.append((q, k, q, k) if w.in_place else (q, k, torch.empty_like(q), torch.empty_like(k)))
+    del q0, k0
+    out = {"workload": "%s: T=%d, q rows %d, k rows %d, e4m3 in/out, bf16 weights%s" % (
+        name, w.T, w.hq, w.hk, ", in place" if w.in_place else ""),
+        "algorithmic_bytes": w.algorithmic_bytes()}
+    for K in w.slices:
+        def step(i, K=K):
+            q, k, yq, yk = sets[i % nsets]
+            qk.forward(q, k, gq, gk, eps=w.eps, num_slices=K, out_q=yq, out_k=yk, ctx=ctx, stream=stream)
+        for i in range(args.warmup):
+            step(i)
+        ms = timed(args.steps, step)[0]
+        gbs = w.algorithmic_bytes() / (ms * 1e-3) / 1e9
+        out["K%d" % K] = {"kernel_us": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3), "gbs": gbs,
+                          "frac": gbs / HBM_PEAK_GBS}
+    del sets
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():

@@ -1,0 +1,21 @@
+"""The C ABI from a C++ caller (tests/c_abi_check.cpp): device buffers from
+hipMalloc, the fused forward, the inverse RMS and the split path against the
+fp64 oracle, and the documented error codes, with no Python in between."""
+import os
+import subprocess
+
+import pytest
+
+import c_abi_build
+
+pytestmark = pytest.mark.gpu
+
+
+def test_c_caller():
+    if not os.path.exists(c_abi_build.EXE):  # normally built by __graft_entry__.build()
+        c_abi_build.build()
+    print("[case] c_abi_check", flush=True)
+    out = subprocess.run([c_abi_build.EXE], capture_output=True, text=True, timeout=120)
+    print(out.stdout, flush=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "c_abi_check: ok" in out.stdout
