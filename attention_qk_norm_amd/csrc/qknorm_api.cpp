@@ -354,10 +354,37 @@ void share_gamma(qkn::Seg* s, int dtype) {
   s->lds_gamma = (s->rows_per_wg > 1 && gamma_bytes(s->row_bytes, dtype) <= kLdsGammaMax) ? 1 : 0;
 }
 
+// Statistics-only launches (partial sums, inverse RMS) over rows of at most
+// 2 slots, one wavefront each, and many of them (16 or more per SIMD): each
+// wavefront takes 4 rows (1 slot) or 2 rows (2 slots) at once, so it keeps 4
+// or 2 times the loads in flight. A read-only pass has no stores to overlap
+// its load latency with: 16384 rows of 1024 bf16 columns 8.16 -> 6.97 us,
+// 32768 of 512: 8.52 -> 7.48 us, 16384 of 2048 fp8: 7.49 -> 7.13 us. Passes
+// that also write were neutral to 4% slower and keep one row per wavefront.
+void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
+  for (int i = 0; i < nseg; ++i) a->seg[i].rpw = 1;
+  v->rpw = 1;
+  if (v->mode != qkn::MODE_STATS || v->masked || v->nw != 4 || v->pipe || ctx->opt.max_workgroups > 0 ||
+      ctx->opt.waves_per_row != 0)
+    return;
+  int slots = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (a->seg[i].wpr_log2 != 0 || a->seg[i].nslot > 2) return;
+    slots = a->seg[i].nslot > slots ? a->seg[i].nslot : slots;
+  }
+  if (a->T * nseg < int64_t{16} * 4 * ctx->num_cus) return;
+  v->rpw = slots == 1 ? 4 : 2;
+  for (int i = 0; i < nseg; ++i) {
+    a->seg[i].rpw = v->rpw;
+    a->seg[i].nwg = static_cast<int32_t>(ceil_div(a->T, int64_t{a->seg[i].rows_per_wg} * v->rpw));
+  }
+}
+
 // Enqueue `nseg` segments: grid.x covers the larger segment (capped by the
 // persistent-grid option), grid.y selects the segment. A capped forward uses
 // the pipelined variant, whose workgroups prefetch their next rows.
-int run(const qknorm_ctx* ctx, qkn::Variant v, const qkn::Args& a, int nseg, void* stream) {
+int run(const qknorm_ctx* ctx, qkn::Variant v, qkn::Args a, int nseg, void* stream) {
+  rows_per_wave(ctx, &v, &a, nseg);
   int64_t gx = 0;
   unsigned lds = 0;
   for (int i = 0; i < nseg; ++i) {

@@ -613,13 +613,15 @@ __device__ __forceinline__ void gamma_to_lds(const Hot& s, int wave, int lane, u
   }
 }
 
-// Wait for this wavefront's copies (issued before its VPL row loads, so at
-// most VPL loads may stay in flight), then for the whole workgroup's.
-template <class E, int VPL>
+// Wait for this wavefront's copies (issued before its INFLIGHT row loads, so
+// at most that many loads may stay in flight), then for the whole
+// workgroup's.
+template <class E, int VPL, int INFLIGHT = VPL>
 __device__ __forceinline__ void gamma_from_lds(typename E::G (&g)[VPL], const Layout<VPL>& L,
                                                const u32x4* lds_g) {
-  // s_waitcnt with vmcnt = VPL and the lgkm / exp counters left alone
-  __builtin_amdgcn_s_waitcnt((VPL & 0xF) | ((VPL >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  static_assert(INFLIGHT < 64, "vmcnt holds 6 bits");
+  // s_waitcnt with vmcnt = INFLIGHT and the lgkm / exp counters left alone
+  __builtin_amdgcn_s_waitcnt((INFLIGHT & 0xF) | ((INFLIGHT >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < VPL; ++j) g[j] = E::gamma_lds(lds_g, L.off[j] == kOutside ? 0u : (L.off[j] >> 4));
@@ -658,11 +660,52 @@ __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L
   }
 }
 
-template <class E, int V, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE>
+// Narrow rows (at most 2 slots) with one wavefront per row: each wavefront
+// takes RPW consecutive rows at once, so it has RPW times the loads in
+// flight, and the rows share one copy of the weights (when there are
+// weights). Each row is reduced by the wavefront on its own (no LDS).
+template <class E, int V, int NW, int MODE, bool NT, int RPW>
+__device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int wave, int lane, float* part,
+                                          u32x4* lds_g) {
+  int gi = blockIdx.x;
+  int64_t row0 = (static_cast<int64_t>(gi) * s.rows_per_wg + L.team) * RPW;
+  u32x4 d[RPW][V];
+  typename E::G g[V];
+  const bool staged = MODE != MODE_STATS && s.lds_gamma;
+  if (staged) gamma_to_lds<E, V, NW>(s, wave, lane, lds_g);
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+    load_row<E, V, NT>(d[r], row_rsrc<E>(s.x, s.x_stride, row0 + r, row0 + r < s.T, s.row_bytes), L);
+  if constexpr (MODE != MODE_STATS) {
+    if (staged)
+      gamma_from_lds<E, V, V * RPW>(g, L, lds_g);
+    else
+      load_gamma<E, V>(g, s, L);
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+    row_finish<E, V, MODE, false, NT>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false);
+  // grids capped at the hardware limit only
+  for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
+    row0 = (static_cast<int64_t>(gi) * s.rows_per_wg + L.team) * RPW;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      load_row<E, V, NT>(d[r], row_rsrc<E>(s.x, s.x_stride, row0 + r, row0 + r < s.T, s.row_bytes), L);
+    if constexpr (MODE != MODE_STATS) load_gamma<E, V>(g, s, L);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      row_finish<E, V, MODE, false, NT>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false);
+  }
+}
+
+template <class E, int V, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE, int RPW>
 __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wave, int lane, float* part,
                                      u32x4* lds_g) {
   const Layout<V> L(tb, s, wave, lane);
-  if constexpr (MODE == MODE_HEAD) {
+  if constexpr (RPW > 1) {
+    static_assert(!MASKED && !PIPE && MODE != MODE_HEAD, "several rows per wavefront: plain layouts only");
+    body_rows<E, V, NW, MODE, NT, RPW>(s, L, wave, lane, part, lds_g);
+  } else if constexpr (MODE == MODE_HEAD) {
     int gi = blockIdx.x;
     int64_t row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
     u32x4 d[V];
@@ -717,21 +760,21 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
 // a narrower segment (the key rows of a grouped-query layout) runs the body
 // for VPL/2, VPL/4, ... slots instead, chosen by one uniform branch, so it
 // issues no instructions for slots it does not have.
-template <class E, int V, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE>
+template <class E, int V, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE, int RPW>
 __device__ __forceinline__ void dispatch(const Hot& s, const Tables<VPL>& tb, int wave, int lane,
                                          float* part, u32x4* lds_g) {
   if constexpr (V > 1) {
     if (s.nslot <= V / 2) {
-      dispatch<E, V / 2, VPL, NW, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part, lds_g);
+      dispatch<E, V / 2, VPL, NW, MODE, MASKED, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
       return;
     }
   }
-  body<E, V, VPL, NW, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part, lds_g);
+  body<E, V, VPL, NW, MODE, MASKED, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
 }
 
 // blockIdx.y selects the segment (query rows, key rows), so everything a
 // wavefront needs from the kernel arguments is one round of scalar loads.
-template <class E, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE>
+template <class E, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE, int RPW = 1>
 __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   __shared__ float part[NW * kWave];  // per-wavefront slice partials (teams of > 1 wave)
   extern __shared__ u32x4 lds_g[];    // staged gamma (dynamic size: the launch's widest row)
@@ -740,12 +783,27 @@ __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   const Seg& seg = a.seg[blockIdx.y];
   const Hot s(a, seg);
   const Tables<VPL> tb(seg);
-  dispatch<E, VPL, VPL, NW, MODE, MASKED, NT, PIPE>(s, tb, wave, lane, part, lds_g);
+  dispatch<E, VPL, VPL, NW, MODE, MASKED, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
+}
+
+// Several rows per wavefront (statistics-only launches): slot counts 1 and
+// 2, 4-wavefront workgroups.
+template <class E, int VPL, int RPW>
+hipError_t launch_rows(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
+  if (v.mode != MODE_STATS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((qknorm_kernel<E, VPL, 4, MODE_STATS, false, true, false, RPW>), gd, dim3(4 * kWave), lds, st,
+                     a);
+  return hipGetLastError();
 }
 
 template <class E, int VPL, int NW>
 hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
   const dim3 bd(NW * kWave);
+  if constexpr (NW == 4 && VPL <= 2) {
+    if (v.rpw == 2) return launch_rows<E, VPL, 2>(v, a, gd, lds, st);
+    if (v.rpw == 4) return launch_rows<E, VPL, 4>(v, a, gd, lds, st);
+  }
+  if (v.rpw != 1) return hipErrorInvalidValue;
   if (v.mode == MODE_FWD) {
     if constexpr (NW == 4) {
       if (v.pipe) {

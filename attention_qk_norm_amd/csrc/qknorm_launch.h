@@ -71,6 +71,7 @@ struct Seg {
   int32_t emit_rinv;      // STATS: write 1 / sqrt(S / h + eps) instead of S
   int32_t grouped;        // masked layout whose slices are aligned lane groups of
   int32_t group_log2;     //   2^group_log2 (<= 32) vectors: group sums, no masks
+  int32_t rpw;            // rows each one-wavefront team takes at once (1, 2, 4)
   int32_t slot_base[kMaxSlots];
   int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
 };
@@ -101,6 +102,7 @@ struct Variant {
   bool masked;   // FWD, STATS: masked layout
   bool nt;       // FWD only: non-temporal row loads and stores
   bool pipe;     // FWD only: persistent workgroups with the next rows prefetched
+  int rpw = 1;   // rows per one-wavefront team (1, or 2 / 4 for rows of at most 2 slots)
 };
 
 // Slot counts the kernels are compiled for, per workgroup size.

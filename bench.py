@@ -210,6 +210,24 @@ def secondary(torch, qk, workloads, w, args, K, sets, gq, gk, ctx, stream, dev, 
     extra["copy_same_bytes_us"] = copy_ms * 1e3
     extra["copy_same_bytes_gbs"] = 2 * nb / (copy_ms * 1e-3) / 1e9
 
+    # host cost of one C call (validation, planning, launch) with the
+    # arguments marshalled once, as a C caller would pass them
+    import ctypes
+    q, k, yq, yk = sets[0]
+    L = qk.lib()
+    rq = qk.Rows(q.data_ptr(), yq.data_ptr(), w.hq, w.hq, w.hq)
+    rk = qk.Rows(k.data_ptr(), yk.data_ptr(), w.hk, w.hk, w.hk)
+    dt = qk._dtype_code(q)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    n_host = min(args.steps, 200)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_host):
+        L.qknorm_forward(ctx.handle, dt, w.T, ctypes.byref(rq), ctypes.byref(rk), gq.data_ptr(), gk.data_ptr(),
+                         ctypes.c_float(w.eps), K, sp)
+    extra["host_c_call_us"] = (time.perf_counter() - t0) * 1e6 / n_host
+    torch.cuda.synchronize()
+
     # host view of one call: enqueue, then wait for completion (decode latency)
     lat = []
     for i in range(min(args.steps, 200)):

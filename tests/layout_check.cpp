@@ -138,6 +138,22 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
                 (long long)hk, K, forced_wpr, dtype);
   CHECK(vpl > 0, "%s no compiled variant for %d slots", what, slots);
   if (vpl == 0) return;
+  // several rows per wavefront: every row covered once, no spare workgroups
+  {
+    qkn::Variant v{dtype, qkn::MODE_STATS, vpl, nw, masked, true, false};  // the launches that use it
+    qkn::Args a{};
+    a.T = T;
+    for (int i = 0; i < nseg; ++i) a.seg[i] = seg[i];
+    rows_per_wave(&ctx, &v, &a, nseg);
+    for (int i = 0; i < nseg; ++i) {
+      const int64_t per_wg = int64_t{a.seg[i].rows_per_wg} * a.seg[i].rpw;
+      CHECK(a.seg[i].rpw == v.rpw && (v.rpw == 1 || v.rpw == 2 || v.rpw == 4), "%s rpw %d", what, v.rpw);
+      CHECK(int64_t{a.seg[i].nwg} * per_wg >= T && int64_t{a.seg[i].nwg - 1} * per_wg < T, "%s nwg %d", what,
+            a.seg[i].nwg);
+      CHECK(v.rpw == 1 || (a.seg[i].wpr_log2 == 0 && a.seg[i].nslot * v.rpw <= 4 && !masked && nw == 4),
+            "%s rpw %d with wpr_log2 %d, %d slots", what, v.rpw, a.seg[i].wpr_log2, a.seg[i].nslot);
+    }
+  }
   for (int i = 0; i < nseg; ++i) {
     check_seg(seg[i], nw, vpl, in[i].nvec, K, masked, what);
     // grouped: every slice is one aligned lane group of one slot, in order
@@ -205,7 +221,7 @@ int main() {
   int cases = 0;
   const int64_t widths[] = {8, 24, 64, 96, 200, 256, 512, 1000, 1024, 1032, 1280, 1536, 2048,
                             4096, 5120, 8192, 12288, 16384, 32768, 65536};
-  const int64_t rows[] = {1, 3, 64, 256, 2048, 16384};
+  const int64_t rows[] = {1, 3, 64, 256, 2048, 16384, 20001};
   const int ks[] = {1, 2, 3, 4, 5, 8, 10, 16, 24, 32, 40, 48, 64};
   const int wprs[] = {0, 1, 2, 4, 8, 16};
   for (int dtype : {QKNORM_BF16, QKNORM_F32, QKNORM_FP8_E4M3})

@@ -524,3 +524,57 @@ def test_inv_rms_worked_example_and_strided_rows():
     assert_parity(out[0], oracle.inv_rms(host[:, :Hq], 1e-6, 1), torch.float32, "q")
     assert_parity(out[2], oracle.inv_rms(host[:, Hq:Hq + Hk], 1e-6, 1), torch.float32, "k")
     assert (out[1] == -1.0).all()
+
+
+# ---- several narrow rows per wavefront -----------------------------------------
+
+ROWS_PER_WAVE = [
+    # dtype, T, Hq, Hk, K: rows of 1 or 2 slots and 16 or more rows per SIMD,
+    # so each wavefront takes 4 or 2 rows; T not a multiple of the rows per
+    # workgroup
+    ("bf16", 9001, 1024, 512, 1),
+    ("bf16", 9001, 1024, 512, 2),
+    ("f32", 20001, 256, None, 1),
+    ("f32", 17003, 512, 128, 4),
+    ("fp8", 17000, 1024, 2048, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,T,Hq,Hk,K", ROWS_PER_WAVE)
+def test_rows_per_wavefront(dtype, T, Hq, Hk, K):
+    gdt = "bf16" if dtype == "fp8" else dtype
+    q = workloads.random_rows(T, Hq, dtype, [T, Hq, 5], dist="laplace")
+    k = workloads.random_rows(T, Hk, dtype, [T, Hk, 6]) if Hk else None
+    gq = workloads.random_weights(Hq, gdt, [Hq, 7])
+    gk = workloads.random_weights(Hk, gdt, [Hk, 8]) if Hk else None
+    say("rows per wavefront", dtype, T, Hq, Hk, K)
+    yq, yk = run_forward(q, k, gq, gk, 1e-6, K)
+    assert_parity(yq, oracle.forward(q, gq, 1e-6, K)[0], workloads.DTYPES[dtype], "q")
+    if Hk:
+        assert_parity(yk, oracle.forward(k, gk, 1e-6, K)[0], workloads.DTYPES[dtype], "k")
+    rq, _ = qk.inv_rms(gpu(q), eps=1e-6, num_slices=K)
+    torch.cuda.synchronize()
+    assert_parity(rq, oracle.inv_rms(q, 1e-6, K), torch.float32, "rinv")
+
+
+def test_split_path_on_a_rank_slice():
+    """One rank's share of C5 under 8-way column slicing: slices of 512
+    columns of 4096-wide rows, 16384 tokens (each wavefront takes 4 rows)."""
+    T, H, K = 16384, 4096, 8
+    w = H // K
+    x = workloads.random_rows(T, H, "bf16", 97, dist="laplace")
+    g = workloads.random_weights(H, "bf16", 98)
+    ref, _ = oracle.forward(x, g, 1e-6, K)
+    P = oracle.slice_sumsq(x, K)
+    xd, gd = gpu(x), gpu(g)
+    stats = torch.zeros((K, T), dtype=torch.float32, device=DEV)
+    say("rank slice partial stats")
+    for s in range(K):
+        qk.partial_stats(xd[:, s * w:(s + 1) * w], s, K, stats)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(stats.cpu().double().numpy(), P, rtol=2e-6)
+    for s in (0, 5, 7):
+        say("rank slice apply", s)
+        ys = qk.apply_stats(xd[:, s * w:(s + 1) * w], gd[s * w:(s + 1) * w], stats, H, eps=1e-6)
+        torch.cuda.synchronize()
+        assert_parity(ys, ref[:, s * w:(s + 1) * w], torch.bfloat16, "slice %d" % s)
