@@ -6,7 +6,7 @@ tensors it returns.
 
 The five workloads stand in for the projected query/key activations of the
 OLMo-series models the SwiftQK review evaluates (section 4: OLMoE-7B,
-OLMo2-13B, OLMo3-32B; Fig. 2(a) measures at 64 and 4096 input tokens). The
+OLMo2-13B, OLMo3-32B; Fig. 2(a) uses inputs of 64 and of 4096 tokens). The
 pages' activations come from vLLM serving ShareGPT traffic; neither the
 weights nor the dataset are available, so seeded draws of the same shapes
 and value spreads are used instead.
