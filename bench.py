@@ -68,7 +68,7 @@ def parse():
     p.add_argument("--rotate-mib", type=int, default=2048,
                    help="total size of the rotated buffer sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
+    p.add_argument("--cpu-seconds", type=float, default=16.0,
                    help="approximate CPU time spent timing the oracle")
     p.add_argument("--waves-per-row", type=int, default=0)
     p.add_argument("--max-workgroups", type=int, default=0)
