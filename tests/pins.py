@@ -213,6 +213,22 @@ def pin_brute_force_rows():
             assert abs(P[:, t].sum() - float(exact.sum_of_squares(x[t]))) <= 1e-15 * P[:, t].sum()
 
 
+def pin_tiny_workload_exact():
+    """The tiny fp32 workload (4 tokens, rows of 256) row by row against exact
+    arithmetic, for both of its slice counts and both tensors."""
+    d = workloads.generate("c1")
+    w = d["w"]
+    eps = oracle.eps_as_gpu_sees_it(w.eps)
+    for which in ("q", "k"):
+        x = oracle.as_f32(d[which])
+        g = oracle.as_f32(d["gamma_" + which])
+        refs = [[float(v) for v in exact.rmsnorm_row(x[t], g, eps)] for t in range(w.T)]
+        for K in w.slices:
+            y, _ = oracle.forward(x, g, w.eps, K)
+            for t in range(w.T):
+                np.testing.assert_allclose(y[t], refs[t], rtol=1e-15, atol=0)
+
+
 def pin_library_rms_norm():
     """torch.nn.functional.rms_norm in float64 is an independent textbook
     implementation of Eq. 1."""
@@ -330,6 +346,7 @@ ALL_PINS = [
     pin_unit_rms,
     pin_special_cases,
     pin_brute_force_rows,
+    pin_tiny_workload_exact,
     pin_library_rms_norm,
     pin_headwise_closed_form,
     pin_headwise_exact_rows,
