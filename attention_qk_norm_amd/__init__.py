@@ -12,6 +12,15 @@ calls raise.
 normalises every row of q [T, Hq] and of k [T, Hk] over its full width
 (SwiftQK technical review, Eq. 1), forming each row's sum of squares as the
 ascending sum of `num_slices` per-slice partials (section 4b, Eqs. 3-6).
+The other entry points:
+
+    forward_headwise(q, k, hgamma_q, hgamma_k, head_dim)   one statistic per head
+    inv_rms(q, k)                                           the per-token 1 / RMS alone
+    partial_stats(x_slice, slice_index, num_slices)         split path, step 1
+    apply_stats(x_slice, gamma_slice, stats, h_total)       split path, step 2
+
+Rows are float32, bfloat16 or float8_e4m3fn (with bfloat16 weights); q and
+k may be strided views, such as the column blocks of a packed QKV tensor.
 """
 import ctypes
 import os
