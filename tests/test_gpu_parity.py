@@ -578,3 +578,32 @@ def test_split_path_on_a_rank_slice():
         ys = qk.apply_stats(xd[:, s * w:(s + 1) * w], gd[s * w:(s + 1) * w], stats, H, eps=1e-6)
         torch.cuda.synchronize()
         assert_parity(ys, ref[:, s * w:(s + 1) * w], torch.bfloat16, "slice %d" % s)
+
+
+def test_denormal_statistics():
+    """Rows whose mean of squares is a denormal fp32 value: three entries of
+    +-2^-60 in 256 columns (squares 2^-120, normal and exact) and eps = 2^-130,
+    so mean + eps = 13 * 2^-130 exactly. The inverse RMS must still be the
+    finite one (the hardware reciprocal square root alone would give
+    infinity), for the statistic alone, the layerwise and the headwise form
+    (whose empty heads have mean + eps = 2^-130)."""
+    T, H, D = 6, 256, 64
+    rng = np.random.default_rng(99)
+    x = np.zeros((T, H), np.float32)
+    for t in range(T):
+        cols = rng.choice(H, 3, replace=False)
+        x[t, cols] = np.float32(2.0 ** -60) * rng.choice([-1.0, 1.0], 3).astype(np.float32)
+    x = torch.from_numpy(x)
+    eps = 2.0 ** -130
+    g = workloads.random_weights(H, "f32", 100)
+    xd = gpu(x)
+    say("denormal statistics")
+    r, _ = qk.inv_rms(xd, eps=eps)
+    y, _ = qk.forward(xd, None, gpu(g), None, eps=eps)
+    yh, _ = qk.forward_headwise(xd, None, gpu(g[:D]), None, D, eps=eps)
+    torch.cuda.synchronize()
+    ref = oracle.inv_rms(x, eps, 1)
+    assert (1.0 / (ref * ref) < 2.0 ** -126).all(), "the case must reach denormal means"
+    assert_parity(r, ref, torch.float32, "rinv")
+    assert_parity(y, oracle.forward(x, g, eps, 1)[0], torch.float32, "forward")
+    assert_parity(yh, oracle.headwise(x, g[:D], D, eps), torch.float32, "headwise")
