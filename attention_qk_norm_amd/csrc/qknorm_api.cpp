@@ -361,22 +361,35 @@ void share_gamma(qkn::Seg* s, int dtype) {
 // its load latency with: 16384 rows of 1024 bf16 columns 8.16 -> 6.97 us,
 // 32768 of 512: 8.52 -> 7.48 us, 16384 of 2048 fp8: 7.49 -> 7.13 us. Passes
 // that also write were neutral to 4% slower and keep one row per wavefront.
+//
+// FP8 forward launches that are a single round of one-wavefront rows (fewer
+// than 8 rows per SIMD, at most 8 slots) take 2 rows per wavefront: FP8 rows
+// cost much VALU work (conversions), and with one round there are no other
+// wavefronts to overlap it with memory; a wavefront finishing its first row
+// while its second loads does. C4-fp8 (2048 rows of 5120 + 1024): 8.0 ->
+// 7.15 us. With several rounds the other wavefronts already overlap it
+// (C5-fp8: 46.1 us, against 46.9 with 2 rows).
 void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
   for (int i = 0; i < nseg; ++i) a->seg[i].rpw = 1;
   v->rpw = 1;
-  if (v->mode != qkn::MODE_STATS || v->masked || v->nw != 4 || v->pipe || ctx->opt.max_workgroups > 0 ||
-      ctx->opt.waves_per_row != 0)
-    return;
+  if (v->masked || v->nw != 4 || v->pipe || ctx->opt.max_workgroups > 0 || ctx->opt.waves_per_row != 0) return;
   int slots = 0;
   for (int i = 0; i < nseg; ++i) {
-    if (a->seg[i].wpr_log2 != 0 || a->seg[i].nslot > 2) return;
+    if (a->seg[i].wpr_log2 != 0) return;
     slots = a->seg[i].nslot > slots ? a->seg[i].nslot : slots;
   }
-  if (a->T * nseg < int64_t{16} * 4 * ctx->num_cus) return;
-  v->rpw = slots == 1 ? 4 : 2;
+  const int64_t simds = int64_t{4} * ctx->num_cus;
+  int rpw = 1;
+  if (v->mode == qkn::MODE_STATS && slots <= 2 && a->T * nseg >= 16 * simds)
+    rpw = slots == 1 ? 4 : 2;
+  else if (v->mode == qkn::MODE_FWD && v->dtype == QKNORM_FP8_E4M3 && v->nt && slots <= 8 &&
+           a->T * nseg < 8 * simds)
+    rpw = 2;
+  if (rpw == 1) return;
+  v->rpw = rpw;
   for (int i = 0; i < nseg; ++i) {
-    a->seg[i].rpw = v->rpw;
-    a->seg[i].nwg = static_cast<int32_t>(ceil_div(a->T, int64_t{a->seg[i].rows_per_wg} * v->rpw));
+    a->seg[i].rpw = rpw;
+    a->seg[i].nwg = static_cast<int32_t>(ceil_div(a->T, int64_t{a->seg[i].rows_per_wg} * rpw));
   }
 }
 

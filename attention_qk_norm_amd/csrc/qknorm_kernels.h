@@ -669,10 +669,10 @@ __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L
   }
 }
 
-// Narrow rows (at most 2 slots) with one wavefront per row: each wavefront
-// takes RPW consecutive rows at once, so it has RPW times the loads in
-// flight, and the rows share one copy of the weights (when there are
-// weights). Each row is reduced by the wavefront on its own (no LDS).
+// One wavefront per row, RPW consecutive rows per wavefront: all their loads
+// go out first, then the rows are finished in order, so the work on one row
+// overlaps the loads of the next; the rows share one copy of the weights.
+// Each row is reduced by the wavefront on its own (no LDS).
 template <class E, int V, int NW, int MODE, bool NT, int RPW>
 __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int wave, int lane, float* part,
                                           u32x4* lds_g) {
@@ -795,22 +795,34 @@ __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   dispatch<E, VPL, VPL, NW, MODE, MASKED, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
 }
 
-// Several rows per wavefront (statistics-only launches): slot counts 1 and
-// 2, 4-wavefront workgroups.
+// Several rows per wavefront, 4-wavefront workgroups: statistics-only
+// launches over rows of 1 or 2 slots (2 or 4 rows), and FP8 forward launches
+// of a single round of wavefronts (2 rows, up to 8 slots).
 template <class E, int VPL, int RPW>
 hipError_t launch_rows(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
-  if (v.mode != MODE_STATS) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((qknorm_kernel<E, VPL, 4, MODE_STATS, false, true, false, RPW>), gd, dim3(4 * kWave), lds, st,
-                     a);
-  return hipGetLastError();
+  const dim3 bd(4 * kWave);
+  if (v.mode == MODE_STATS) {
+    if constexpr (VPL <= 2) {
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, 4, MODE_STATS, false, true, false, RPW>), gd, bd, lds, st, a);
+      return hipGetLastError();
+    }
+  } else if (v.mode == MODE_FWD && v.nt) {
+    if constexpr (E::kDtype == QKNORM_FP8_E4M3 && RPW == 2) {
+      hipLaunchKernelGGL((qknorm_kernel<E, VPL, 4, MODE_FWD, false, true, false, RPW>), gd, bd, lds, st, a);
+      return hipGetLastError();
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <class E, int VPL, int NW>
 hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
   const dim3 bd(NW * kWave);
-  if constexpr (NW == 4 && VPL <= 2) {
+  if constexpr (NW == 4) {
     if (v.rpw == 2) return launch_rows<E, VPL, 2>(v, a, gd, lds, st);
-    if (v.rpw == 4) return launch_rows<E, VPL, 4>(v, a, gd, lds, st);
+    if constexpr (VPL <= 2) {
+      if (v.rpw == 4) return launch_rows<E, VPL, 4>(v, a, gd, lds, st);
+    }
   }
   if (v.rpw != 1) return hipErrorInvalidValue;
   if (v.mode == MODE_FWD) {

@@ -139,8 +139,8 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
   CHECK(vpl > 0, "%s no compiled variant for %d slots", what, slots);
   if (vpl == 0) return;
   // several rows per wavefront: every row covered once, no spare workgroups
-  {
-    qkn::Variant v{dtype, qkn::MODE_STATS, vpl, nw, masked, true, false};  // the launches that use it
+  for (int mode : {qkn::MODE_STATS, qkn::MODE_FWD}) {
+    qkn::Variant v{dtype, mode, vpl, nw, masked, true, false};
     qkn::Args a{};
     a.T = T;
     for (int i = 0; i < nseg; ++i) a.seg[i] = seg[i];
@@ -150,8 +150,10 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
       CHECK(a.seg[i].rpw == v.rpw && (v.rpw == 1 || v.rpw == 2 || v.rpw == 4), "%s rpw %d", what, v.rpw);
       CHECK(int64_t{a.seg[i].nwg} * per_wg >= T && int64_t{a.seg[i].nwg - 1} * per_wg < T, "%s nwg %d", what,
             a.seg[i].nwg);
-      CHECK(v.rpw == 1 || (a.seg[i].wpr_log2 == 0 && a.seg[i].nslot * v.rpw <= 4 && !masked && nw == 4),
-            "%s rpw %d with wpr_log2 %d, %d slots", what, v.rpw, a.seg[i].wpr_log2, a.seg[i].nslot);
+      CHECK(v.rpw == 1 || (a.seg[i].wpr_log2 == 0 && !masked && nw == 4 &&
+                           (mode == qkn::MODE_STATS ? a.seg[i].nslot * v.rpw <= 4
+                                                    : dtype == QKNORM_FP8_E4M3 && v.rpw == 2 && a.seg[i].nslot <= 8)),
+            "%s mode %d rpw %d with wpr_log2 %d, %d slots", what, mode, v.rpw, a.seg[i].wpr_log2, a.seg[i].nslot);
     }
   }
   for (int i = 0; i < nseg; ++i) {

@@ -80,6 +80,7 @@ SHAPES = [
     (9, 3072, 1536, 48),       # slices of 64 and 32 elements: masked layout
     (2, 65536, 16, 1),         # widest fp8 row
     (3000, 512, 128, 2),       # many rows per SIMD
+    (2001, 5120, 1024, 1),     # one round of wavefronts, 2 rows each; ragged T
 ]
 
 
