@@ -75,9 +75,6 @@ struct SameTypeGamma {
     return load16<false>(r, off);
   }
   static __device__ __forceinline__ G gamma_lds(const u32x4* lds, uint32_t v) { return lds[v]; }
-  // fp32 and bf16 results cannot leave their type's range here
-  template <int V>
-  static __device__ __forceinline__ bool may_saturate(const G (&)[V], float) { return false; }
 };
 
 // binary32 rows: 4 elements per 16-byte vector.
@@ -92,8 +89,9 @@ struct F32 : SameTypeGamma {
     }
     return acc;
   }
+  static constexpr bool kSaturates = false;
   template <bool SAT>
-  static __device__ __forceinline__ u32x4 scale(u32x4 d, u32x4 g, float r) {
+  static __device__ __forceinline__ u32x4 encode(u32x4 d, u32x4 g, float r, float&) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -122,8 +120,9 @@ struct BF16 : SameTypeGamma {
     }
     return acc;
   }
+  static constexpr bool kSaturates = false;
   template <bool SAT>
-  static __device__ __forceinline__ u32x4 scale(u32x4 d, u32x4 g, float r) {
+  static __device__ __forceinline__ u32x4 encode(u32x4 d, u32x4 g, float r, float&) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -148,15 +147,6 @@ struct BF16 : SameTypeGamma {
 __device__ __forceinline__ f32x2 fp8_pair(uint32_t w, bool high) {
   return high ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true)
               : __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-}
-
-// The raw word, hidden from the optimiser: the scaling pass decodes the row
-// again instead of keeping 16 decoded floats per vector alive across the
-// reduction (which costs about 12 more VGPRs per slot than the decode
-// costs in instructions). The empty asm emits nothing.
-__device__ __forceinline__ uint32_t opaque(uint32_t w) {
-  asm volatile("" : "+v"(w));
-  return w;
 }
 
 __device__ __forceinline__ float sat_e4m3(float v) {
@@ -191,35 +181,12 @@ struct FP8 {
     }
     return acc;
   }
-  // Can any result of this wavefront pass 448? |x_j r| <= sqrt(h) because
-  // x_j^2 <= S (fp32 rounding of S and of the products stays far inside the
-  // 2^-10 margin), so |y_j| <= sqrt(h) * max|gamma|. When even that bound
-  // stays below 448 the clamp is skipped. The largest |gamma| is taken on
-  // the bf16 bits (non-negative bf16 values order like 16-bit integers; a
-  // NaN weight counts as huge), one packed integer max per weight dword.
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  // by value, for the same reason as as_bf16x2
-  static __device__ __forceinline__ u16x2 magnitudes(uint32_t w) {
-    return __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
-  }
-  template <int V>
-  static __device__ __forceinline__ bool may_saturate(const G (&g)[V], float h) {
-    u16x2 m = {0, 0};
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        m = __builtin_elementwise_max(m, magnitudes(g[j].lo[i]));
-        m = __builtin_elementwise_max(m, magnitudes(g[j].hi[i]));
-      }
-    }
-    const uint32_t top = m.x > m.y ? m.x : m.y;
-    const float gmax = __uint_as_float(top << 16);
-    const bool lane = !(gmax * __builtin_sqrtf(h) * (1.0f + 0x1p-10f) <= 448.0f);
-    return __builtin_amdgcn_ballot_w64(lane) != 0;
-  }
+  // y = (x r) gamma for the vector's 16 elements, rounded to nearest-even
+  // e4m3. SAT: results past 448 (infinities included) become +-448 first.
+  // Otherwise `peak` takes the largest |y| (three-operand maxima; a NaN
+  // result leaves it unchanged and is encoded as NaN).
   template <bool SAT>
-  static __device__ __forceinline__ u32x4 scale(u32x4 d, const G& g, float r) {
+  static __device__ __forceinline__ u32x4 encode(u32x4 d, const G& g, float r, float& peak) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -227,7 +194,7 @@ struct FP8 {
       // 4i..4i+3, i.e. weight dwords 2i and 2i+1
       const uint32_t g0 = i < 2 ? g.lo[2 * i] : g.hi[2 * i - 4];
       const uint32_t g1 = i < 2 ? g.lo[2 * i + 1] : g.hi[2 * i - 3];
-      const uint32_t w8 = opaque(d[i]);
+      const uint32_t w8 = d[i];
       const f32x2 a = fp8_pair(w8, false);
       const f32x2 b = fp8_pair(w8, true);
       float y0 = a.x * r * __uint_as_float(g0 << 16);
@@ -239,12 +206,47 @@ struct FP8 {
         y1 = sat_e4m3(y1);
         y2 = sat_e4m3(y2);
         y3 = sat_e4m3(y3);
+      } else {
+        peak = __builtin_fmaxf(__builtin_fmaxf(peak, __builtin_fabsf(y0)), __builtin_fabsf(y1));
+        peak = __builtin_fmaxf(__builtin_fmaxf(peak, __builtin_fabsf(y2)), __builtin_fabsf(y3));
       }
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      // both halves are written, so the word the conversion starts from is
+      // immaterial: the input word saves an initialisation
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, static_cast<int>(w8), false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
       o[i] = static_cast<uint32_t>(w);
     }
     return o;
+  }
+  // The plain encoding saturates nothing (past 464 it gives NaN): rows are
+  // encoded plainly, and a lane whose results passed 448 encodes and writes
+  // its vectors again with the clamp (encode_store).
+  static constexpr bool kSaturates = true;
+  // Whether the weights alone keep every result of rows of width h inside
+  // the range: |x_j r| <= sqrt(h) since x_j^2 <= S (fp32 rounding of S and of
+  // the products stays far inside the 2^-10 margin), so |y_j| <= sqrt(h)
+  // max|gamma|. The largest |gamma| is taken on the bf16 bits (non-negative
+  // bf16 values order like 16-bit integers; a NaN weight counts as huge),
+  // one packed integer maximum per weight dword; uniform over the wavefront.
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ u16x2 magnitudes(uint32_t w) {  // by value, as as_bf16x2
+    return __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+  }
+  template <int V>
+  static __device__ __forceinline__ bool weights_bound(const G (&g)[V], float h) {
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = __builtin_elementwise_max(m, magnitudes(g[j].lo[i]));
+        m = __builtin_elementwise_max(m, magnitudes(g[j].hi[i]));
+      }
+    }
+    const uint32_t top = m.x > m.y ? m.x : m.y;
+    const float gmax = __uint_as_float(top << 16);
+    const bool lane = gmax * __builtin_sqrtf(h) * (1.0f + 0x1p-10f) <= 448.0f;
+    return __builtin_amdgcn_ballot_w64(!lane) == 0;
   }
 };
 
@@ -534,26 +536,59 @@ __device__ __forceinline__ float inv_rms(float S, float h, float eps) {
   return rsqrt_full(S / h + eps);
 }
 
-// BOUNDED: S covers every element scaled here (not so for partials handed in
-// by a caller), so |x r| <= sqrt(h) and the weights alone decide whether a
-// result can saturate.
-template <class E, int VPL, bool NT, bool BOUNDED>
-__device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], float S,
-                                            float h, float eps, __amdgpu_buffer_rsrc_t yr,
-                                            const Layout<VPL>& L) {
-  const float r = inv_rms(S, h, eps);
-  if (!BOUNDED || E::may_saturate(g, h)) {
+// Scale and store a lane's vectors: vector j with weights gw(j) and inverse
+// RMS rw(j). Types that saturate (FP8) are encoded plainly while each
+// vector's largest |y| is tracked; a vector with a result past the type's
+// range is not stored (its store goes to the dropped offset) but marked,
+// and the lanes with marks then load those input vectors again (still
+// unwritten, also in place) with their weights gr(j), and store them
+// encoded with the clamp. The common case is one straight pass: a compare,
+// a select and an OR per vector, and one branch per row.
+template <class E, int VPL, bool NT, bool CHECK, class GW, class RW, class GR>
+__device__ __forceinline__ void encode_store(const u32x4 (&d)[VPL], GW gw, RW rw, GR gr,
+                                             __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t yr,
+                                             const Layout<VPL>& L) {
+  uint32_t redo = 0;
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::template scale<true>(d[j], g[j], r));
-  } else {
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) store16<NT>(yr, L.off[j], E::template scale<false>(d[j], g[j], r));
+  for (int j = 0; j < VPL; ++j) {
+    float peak = 0.f;
+    const u32x4 o = E::template encode<false>(d[j], gw(j), rw(j), peak);
+    if constexpr (CHECK) {
+      const bool over = peak > 448.0f;
+      redo |= over ? 1u << j : 0u;
+      store16<NT>(yr, over ? kOutside : L.off[j], o);
+    } else {
+      store16<NT>(yr, L.off[j], o);
+    }
   }
+  if constexpr (CHECK) {
+    if (redo != 0) {
+      for (int j = 0; j < VPL; ++j) {
+        if ((redo >> j) & 1u) {
+          float unused = 0.f;
+          const u32x4 x = load16<NT>(xr, L.off[j]);
+          store16<NT>(yr, L.off[j], E::template encode<true>(x, gr(j), rw(j), unused));
+        }
+      }
+    }
+  }
+}
+
+// Row `row` scaled by its statistic S and the per-column weights g.
+template <class E, int VPL, bool NT, bool CHECK = E::kSaturates>
+__device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], float S,
+                                            const Hot& s, int64_t row, bool live, const Layout<VPL>& L) {
+  const float r = inv_rms(S, s.h, s.eps);
+  const auto grs = rsrc(s.gamma, s.row_bytes * E::kGammaScale);
+  encode_store<E, VPL, NT, CHECK>(
+      d, [&](int j) -> const typename E::G& { return g[j]; }, [&](int) { return r; },
+      [&](int j) { return E::load_gamma(grs, L.off[j]); }, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes),
+      row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
 }
 
 // Finish one row whose data (and weights) are in registers: statistic (or
 // the precomputed partials), then scale and store, or publish the statistic.
-template <class E, int VPL, int MODE, bool MASKED, bool NT>
+template <class E, int VPL, int MODE, bool MASKED, bool NT, bool CHECK = E::kSaturates>
 __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], const Hot& s,
                                            const Layout<VPL>& L, int64_t row, bool live, int wave,
                                            int lane, float* part, bool reuse) {
@@ -569,8 +604,7 @@ __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename
   if constexpr (MODE == MODE_STATS) {
     if (live && L.tl == 0) s.stats_out[row] = s.emit_rinv ? inv_rms(S, s.h, s.eps) : S;
   } else {
-    scale_store<E, VPL, NT, MODE != MODE_APPLY>(d, g, S, s.h, s.eps,
-                                                row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
+    scale_store<E, VPL, NT, CHECK>(d, g, S, s, row, live, L);
   }
 }
 
@@ -584,17 +618,12 @@ __device__ __forceinline__ void head_finish(const u32x4 (&d)[VPL], const typenam
 #pragma unroll
   for (int j = 0; j < VPL; ++j) q[j] = E::sumsq(d[j], 0.f);
   head_sums<VPL>(q, s.head_log2, lane);
-  const auto yr = row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes);
-  const typename E::G gs[1] = {g};
-  if (E::may_saturate(gs, s.h)) {
+  float r[VPL];
 #pragma unroll
-    for (int j = 0; j < VPL; ++j)
-      store16<NT>(yr, L.off[j], E::template scale<true>(d[j], g, rsqrt_full(q[j] * s.inv_h + s.eps)));
-  } else {
-#pragma unroll
-    for (int j = 0; j < VPL; ++j)
-      store16<NT>(yr, L.off[j], E::template scale<false>(d[j], g, rsqrt_full(q[j] * s.inv_h + s.eps)));
-  }
+  for (int j = 0; j < VPL; ++j) r[j] = rsqrt_full(q[j] * s.inv_h + s.eps);
+  encode_store<E, VPL, NT, E::kSaturates>(
+      d, [&](int) -> const typename E::G& { return g; }, [&](int j) { return r[j]; }, [&](int) { return g; },
+      row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
 }
 
 // Weights for the team's slots when several rows share a workgroup: the
@@ -657,13 +686,13 @@ __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L
     const int64_t rb = static_cast<int64_t>(g1) * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(B, row_rsrc<E>(s.x, s.x_stride, rb, g1 < s.nwg && rb < s.T, s.row_bytes), L);
     float S = row_stat<E, VPL, MASKED>(A, s, L, wave, lane, part, true);
-    scale_store<E, VPL, NT, true>(A, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, ra, ra < s.T, s.row_bytes), L);
+    scale_store<E, VPL, NT>(A, g, S, s, ra, ra < s.T, L);
     if (g1 >= s.nwg) break;
     const int g2 = g1 + G;
     ra = static_cast<int64_t>(g2) * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(A, row_rsrc<E>(s.x, s.x_stride, ra, g2 < s.nwg && ra < s.T, s.row_bytes), L);
     S = row_stat<E, VPL, MASKED>(B, s, L, wave, lane, part, true);
-    scale_store<E, VPL, NT, true>(B, g, S, s.h, s.eps, row_rsrc<E>(s.y, s.y_stride, rb, rb < s.T, s.row_bytes), L);
+    scale_store<E, VPL, NT>(B, g, S, s, rb, rb < s.T, L);
     if (g2 >= s.nwg) break;
     g0 = g2;
   }
@@ -691,9 +720,20 @@ __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int 
     else
       load_gamma<E, V>(g, s, L);
   }
+  // FP8 forward: when the weights alone bound every result inside the range
+  // (checked once for all the wavefront's rows), the rows skip the
+  // per-vector test. With a single round of wavefronts this is faster.
+  bool check = E::kSaturates;
+  if constexpr (E::kSaturates && MODE == MODE_FWD) check = !E::weights_bound(g, s.h);
+  if (check) {
 #pragma unroll
-  for (int r = 0; r < RPW; ++r)
-    row_finish<E, V, MODE, false, NT>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false);
+    for (int r = 0; r < RPW; ++r)
+      row_finish<E, V, MODE, false, NT>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      row_finish<E, V, MODE, false, NT, false>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false);
+  }
   // grids capped at the hardware limit only
   for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
     row0 = (static_cast<int64_t>(gi) * s.rows_per_wg + L.team) * RPW;

@@ -190,6 +190,45 @@ def test_fp8_schedules(opts):
     assert_parity(yk, oracle.forward(k, gk, 1e-6, K)[0], FP8, "k")
 
 
+@pytest.mark.parametrize("in_place", [False, True], ids=["out", "in_place"])
+@pytest.mark.parametrize("K", [1, 4])
+@pytest.mark.parametrize("opts", [dict(), dict(max_workgroups=5), dict(waves_per_row=2)],
+                         ids=lambda o: ",".join("%s=%s" % kv for kv in o.items()) or "auto")
+def test_fp8_dense_saturation(in_place, K, opts):
+    """Weights of +-(200..600) saturate a large share of every row, in many
+    lanes and every slot at once: each such vector is encoded a second time
+    with the clamp from the input, which in place must still be unwritten.
+    T = 300 rows of q and k is one round of wavefronts (two rows each, with
+    the automatic schedule); a NaN row stays NaN, a zero row zero."""
+    ctx = qk.Context(0, **opts)
+    T, Hq, Hk = 300, 5120, 1024
+    q = rows(T, Hq, [51, K], dist="laplace").float()
+    k = rows(T, Hk, [52, K]).float()
+    q[5, 333] = float("nan")
+    q[6] = 0.0
+    k[7, 1000] = float("nan")
+    q, k = q.to(FP8), k.to(FP8)
+    gq, gk = weights(Hq, 53, 200.0, 600.0).float(), weights(Hk, 54, 200.0, 600.0).float()
+    gq[::3] = -gq[::3]
+    gk[1::2] = -gk[1::2]
+    gq, gk = gq.to(torch.bfloat16), gk.to(torch.bfloat16)
+    keep_q = [t for t in range(T) if t != 5]
+    keep_k = [t for t in range(T) if t != 7]
+    rq, _ = oracle.forward(q[keep_q], gq, 1e-6, K)
+    rk, _ = oracle.forward(k[keep_k], gk, 1e-6, K)
+    assert (np.abs(rq) >= 464).mean() > 0.05 and (np.abs(rk) >= 464).mean() > 0.05
+    dq, dk = gpu(q), gpu(k)
+    say("fp8 dense saturation", opts, "K=%d" % K, "in_place" if in_place else "out of place")
+    yq, yk = qk.forward(dq, dk, gpu(gq), gpu(gk), eps=1e-6, num_slices=K, ctx=ctx,
+                        out_q=dq if in_place else None, out_k=dk if in_place else None)
+    torch.cuda.synchronize()
+    hq, hk = yq.cpu().float(), yk.cpu().float()
+    assert torch.isnan(hq[5]).all() and torch.isnan(hk[7]).all()
+    assert (hq[6] == 0).all()
+    assert_parity(yq[keep_q], rq, FP8, "q")
+    assert_parity(yk[keep_k], rk, FP8, "k")
+
+
 def test_fp8_packed_qkv_in_place():
     T, Hq, Hk, Hv = 45, 2048, 512, 512
     H = Hq + Hk + Hv
