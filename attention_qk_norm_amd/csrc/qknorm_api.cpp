@@ -151,32 +151,45 @@ int check_fused(int dtype, int64_t T, const qknorm_rows* const* segs, const void
 
 // How one segment's rows are spread over lanes.
 struct Plan {
-  int wpr_log2 = 0;  // team: 2^wpr_log2 wavefronts per row
-  int sub_log2 = 0;  // sub-team: 2^sub_log2 wavefronts deal one slice
+  int wpr_log2 = 0;        // team: 2^wpr_log2 wavefronts per row
+  int sub_lanes_log2 = 6;  // sub-team: 2^sub_lanes_log2 lanes deal one slice at a time
   int slots = 0;
   bool masked = false;
 };
 
 // Slots per lane of the segmented layout: teams of 2^wl wavefronts, split
-// into sub-teams of 2^m that take the row's K slices round-robin; each
-// sub-team deals each of its slices over its 64 * 2^m lanes.
-int seg_slots(int64_t slice_vec, int K, int wl, int m) {
-  const int64_t nsub = int64_t{1} << (wl - m);
-  return static_cast<int>(ceil_div(K, nsub) * ceil_div(slice_vec, int64_t{64} << m));
+// into sub-teams of 2^sl lanes that take the row's K slices round-robin;
+// each sub-team deals each of its slices over its lanes.
+int seg_slots(int64_t slice_vec, int K, int wl, int sl) {
+  const int64_t nsub = int64_t{1} << (6 + wl - sl);
+  return static_cast<int>(ceil_div(K, nsub) * ceil_div(slice_vec, int64_t{1} << sl));
 }
 int plain_slots(int64_t nvec, int wl) {
   return static_cast<int>(ceil_div(nvec, int64_t{64} << wl));
 }
+// The masked layout: plain strided slots over the whole team.
+Plan masked_plan(int64_t nvec, int wl) { return Plan{wl, 6 + wl, plain_slots(nvec, wl), true}; }
+// Plans served by the kernels for slices narrower than a wavefront.
+bool narrow_plan(const Plan& p) { return p.masked || p.sub_lanes_log2 < 6; }
 
-// The sub-team size with the fewest slots for a team of 2^wl wavefronts;
-// ties go to the smaller sub-team (fewer partials to combine).
+// The sub-team size with the fewest slots for a team of 2^wl wavefronts.
+// Sub-teams of whole wavefronts come first (ties go to the smaller one:
+// fewer partials to combine through LDS). Narrower ones are taken only when
+// they need fewer slots (many narrow slices); among those, ties go to the
+// narrower, which holds fewer slices per lane one after another (fewer
+// rounds of group sums).
 Plan seg_plan(int64_t slice_vec, int K, int wl) {
-  Plan best{wl, 0, seg_slots(slice_vec, K, wl, 0), false};
-  for (int m = 1; m <= wl; ++m) {
-    const int n = seg_slots(slice_vec, K, wl, m);
-    if (n < best.slots) best = Plan{wl, m, n, false};
+  Plan best{wl, 6, seg_slots(slice_vec, K, wl, 6), false};
+  for (int sl = 7; sl <= 6 + wl; ++sl) {
+    const int n = seg_slots(slice_vec, K, wl, sl);
+    if (n < best.slots) best = Plan{wl, sl, n, false};
   }
-  return best;
+  Plan narrow{wl, 5, seg_slots(slice_vec, K, wl, 5), false};
+  for (int sl = 4; sl >= 0; --sl) {
+    const int n = seg_slots(slice_vec, K, wl, sl);
+    if (n <= narrow.slots) narrow = Plan{wl, sl, n, false};
+  }
+  return narrow.slots < best.slots ? narrow : best;
 }
 
 // Choose the team size for one segment by its row width. The smallest team
@@ -195,7 +208,7 @@ bool plan_segment(int64_t nvec, int K, int max_wl, int cap, int forced_wl, Plan*
     // empty: the masked layout then issues half the loads or fewer
     const int m = plain_slots(nvec, wl);
     if (m <= cap && 2 * m <= p.slots) {
-      *out = Plan{wl, wl, m, true};
+      *out = masked_plan(nvec, wl);
       return true;
     }
     if (p.slots <= cap) {
@@ -206,7 +219,7 @@ bool plan_segment(int64_t nvec, int K, int max_wl, int cap, int forced_wl, Plan*
   for (int wl = lo; wl <= hi; ++wl) {
     const int n = plain_slots(nvec, wl);
     if (n <= cap) {
-      *out = Plan{wl, wl, n, true};
+      *out = masked_plan(nvec, wl);
       return true;
     }
   }
@@ -268,7 +281,7 @@ int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int
     if (T * nseg >= 8 * simds) {
       for (int i = 0; i < nseg; ++i) {
         if (plans[i].wpr_log2 != 0 || plans[i].slots < 8) continue;
-        const Plan p = plans[i].masked ? Plan{1, 1, plain_slots(in[i].nvec, 1), true}
+        const Plan p = plans[i].masked ? masked_plan(in[i].nvec, 1)
                                        : seg_plan(in[i].nvec / in[i].K, in[i].K, 1);
         if (p.slots <= cap4) plans[i] = p;
       }
@@ -283,7 +296,7 @@ int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int
       for (int i = 0; i < nseg; ++i) {
         const int wl = plans[i].wpr_log2 + 1;
         if (wl > 2) continue;
-        plans[i] = plans[i].masked ? Plan{wl, wl, plain_slots(in[i].nvec, wl), true}
+        plans[i] = plans[i].masked ? masked_plan(in[i].nvec, wl)
                                    : seg_plan(in[i].nvec / in[i].K, in[i].K, wl);
         widened = true;
       }
@@ -299,12 +312,13 @@ int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int
 // plain strided slots over the whole team.
 void fill_layout(qkn::Seg* s, const Plan& p, int nw, int64_t nvec, int K, int64_t T) {
   const int wl = p.wpr_log2;
-  const int m = p.masked ? wl : p.sub_log2;
-  const int64_t ns = int64_t{64} << m;  // lanes per sub-team
-  const int64_t nsub = int64_t{1} << (wl - m);
+  const int sl = p.sub_lanes_log2;  // the whole team when masked
+  const int64_t ns = int64_t{1} << sl;  // lanes per sub-team
+  const int64_t nsub = int64_t{1} << (6 + wl - sl);
   const int64_t slice_vec = nvec / K;
   s->wpr_log2 = wl;
-  s->sub_log2 = m;
+  s->sub_lanes_log2 = sl;
+  s->masked = p.masked ? 1 : 0;
   s->rows_per_wg = nw >> wl;
   s->nwg = static_cast<int32_t>(ceil_div(T, s->rows_per_wg));
   s->lay_k = K;
@@ -318,13 +332,6 @@ void fill_layout(qkn::Seg* s, const Plan& p, int nw, int64_t nvec, int K, int64_
     s->slot_lim[j] = 0;
   }
   if (p.masked) {
-    // slices of 2^g <= 32 vectors tile each wavefront's 64 lanes exactly
-    s->grouped = 0;
-    s->group_log2 = 0;
-    if (slice_vec <= 32 && (slice_vec & (slice_vec - 1)) == 0) {
-      s->grouped = 1;
-      while ((int64_t{1} << s->group_log2) < slice_vec) ++s->group_log2;
-    }
     s->nslot = static_cast<int32_t>(ceil_div(nvec, ns));
     for (int j = 0; j < s->nslot; ++j) {
       s->slot_base[j] = static_cast<int32_t>(j * ns);
@@ -372,7 +379,7 @@ void share_gamma(qkn::Seg* s, int dtype) {
 void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
   for (int i = 0; i < nseg; ++i) a->seg[i].rpw = 1;
   v->rpw = 1;
-  if (v->masked || v->nw != 4 || v->pipe || ctx->opt.max_workgroups > 0 || ctx->opt.waves_per_row != 0) return;
+  if (v->narrow || v->nw != 4 || v->pipe || ctx->opt.max_workgroups > 0 || ctx->opt.waves_per_row != 0) return;
   int slots = 0;
   for (int i = 0; i < nseg; ++i) {
     if (a->seg[i].wpr_log2 != 0) return;
@@ -499,8 +506,8 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
   st = plan_launch(ctx, dtype, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) return st;
 
-  bool masked = false;
-  for (int i = 0; i < nseg; ++i) masked = masked || plans[i].masked;
+  bool narrow = false;
+  for (int i = 0; i < nseg; ++i) narrow = narrow || narrow_plan(plans[i]);
   qkn::Args a{};
   a.T = T;
   a.eps = eps;
@@ -512,18 +519,16 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
     s.gamma = gammas[i];
     s.x_stride = segs[i]->x_stride;
     s.y_stride = segs[i]->y_stride;
-    // one kernel serves both segments, so a masked plan for either puts both
-    // in the masked layout (never more slots than their segmented plan)
-    Plan pl = plans[i];
-    if (masked && !pl.masked) pl = Plan{pl.wpr_log2, pl.wpr_log2, plain_slots(in[i].nvec, pl.wpr_log2), true};
-    fill_layout(&s, pl, nw, in[i].nvec, num_slices, T);
+    // one kernel serves both segments: the kernels for narrow slices when
+    // either needs them (they also run the other layouts)
+    fill_layout(&s, plans[i], nw, in[i].nvec, num_slices, T);
     share_gamma(&s, dtype);
     s.h = static_cast<float>(segs[i]->width);
     s.comb_k = 0;
     slots = s.nslot > slots ? s.nslot : slots;
   }
-  qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw, dtype), nw, masked,
-                 ctx->opt.cached_rows == 0 || masked, false};
+  qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw, dtype), nw, narrow,
+                 ctx->opt.cached_rows == 0 || narrow, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, nseg, stream);
 }
@@ -557,8 +562,8 @@ int qknorm_forward_headwise(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_
   a.eps = eps;
   int slots = 0;
   for (int i = 0; i < nseg; ++i) {
-    // one slice is never masked: heads rely on the strided layout
-    if (plans[i].masked) return QKNORM_ERR_SHAPE;
+    // one slice is never narrow: heads rely on the strided layout
+    if (narrow_plan(plans[i])) return QKNORM_ERR_SHAPE;
     qkn::Seg& s = a.seg[i];
     s.x = segs[i]->x;
     s.y = segs[i]->y;
@@ -612,8 +617,8 @@ int qknorm_inv_rms(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
   int nw = 4;
   st = plan_launch(ctx, dtype, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) return st;
-  bool masked = false;
-  for (int i = 0; i < nseg; ++i) masked = masked || plans[i].masked;
+  bool narrow = false;
+  for (int i = 0; i < nseg; ++i) narrow = narrow || narrow_plan(plans[i]);
   qkn::Args a{};
   a.T = T;
   a.eps = eps;
@@ -623,14 +628,12 @@ int qknorm_inv_rms(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
     s.x = segs[i]->x;
     s.x_stride = segs[i]->x_stride;
     s.stats_out = outs[i];
-    Plan pl = plans[i];
-    if (masked && !pl.masked) pl = Plan{pl.wpr_log2, pl.wpr_log2, plain_slots(in[i].nvec, pl.wpr_log2), true};
-    fill_layout(&s, pl, nw, in[i].nvec, num_slices, T);
+    fill_layout(&s, plans[i], nw, in[i].nvec, num_slices, T);
     s.h = static_cast<float>(segs[i]->width);
     s.emit_rinv = 1;
     slots = s.nslot > slots ? s.nslot : slots;
   }
-  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(slots, nw, dtype), nw, masked, true, false};
+  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(slots, nw, dtype), nw, narrow, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, nseg, stream);
 }

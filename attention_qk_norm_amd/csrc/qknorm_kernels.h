@@ -289,17 +289,17 @@ struct Hot {
   const float* stats_in;
   float* stats_out;
   int64_t x_stride, y_stride, T;
-  int rows_per_wg, nwg, nslot, wpr_log2, sub_log2, lds_gamma, lay_k, comb_k, slice_vec, head_log2, emit_rinv,
-      grouped, group_log2;
+  int rows_per_wg, nwg, nslot, wpr_log2, sub_lanes_log2, lds_gamma, lay_k, comb_k, masked, slice_vec,
+      head_log2, emit_rinv;
   uint32_t row_bytes, flush_mask;
   float inv_slice_vec, h, inv_h, eps;
 
   __device__ __forceinline__ Hot(const Args& a, const Seg& s)
       : x(s.x), y(s.y), gamma(s.gamma), stats_in(s.stats_in), stats_out(s.stats_out),
         x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
-        nslot(s.nslot), wpr_log2(s.wpr_log2), sub_log2(s.sub_log2), lds_gamma(s.lds_gamma),
-        lay_k(s.lay_k), comb_k(s.comb_k), slice_vec(s.slice_vec), head_log2(s.head_log2), emit_rinv(s.emit_rinv),
-        grouped(s.grouped), group_log2(s.group_log2),
+        nslot(s.nslot), wpr_log2(s.wpr_log2), sub_lanes_log2(s.sub_lanes_log2), lds_gamma(s.lds_gamma),
+        lay_k(s.lay_k), comb_k(s.comb_k), masked(s.masked), slice_vec(s.slice_vec), head_log2(s.head_log2),
+        emit_rinv(s.emit_rinv),
         row_bytes(s.row_bytes), flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h),
         inv_h(s.inv_h), eps(a.eps) {}
 };
@@ -326,7 +326,7 @@ struct Tables {
 
 // Where this lane's V slots sit in a row of one segment: fixed for the whole
 // launch, computed once per wavefront. A team of 2^wpr_log2 wavefronts owns
-// a row; it is split into sub-teams of 2^sub_log2 wavefronts, and the row's
+// a row; it is split into sub-teams of 2^sub_lanes_log2 lanes, and the row's
 // slices are dealt to the sub-teams round-robin, so slices narrower than the
 // team still keep every lane busy.
 template <int V>
@@ -342,11 +342,11 @@ struct Layout {
     wpr = 1 << wpr_log2;
     team = wave >> wpr_log2;
     tl = ((wave & (wpr - 1)) << 6) | lane;  // lane within the team
-    const int sub = (tl >> 6) >> s.sub_log2;
+    const int sub = tl >> s.sub_lanes_log2;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      base[j] = tb.base[j] + sub * s.slice_vec + (tl & ((64 << s.sub_log2) - 1));
-      const int v = slot_vector(tb.lim[j], tb.base[j], tl, wpr_log2, s.sub_log2, s.slice_vec, s.lay_k);
+      base[j] = tb.base[j] + sub * s.slice_vec + (tl & ((1 << s.sub_lanes_log2) - 1));
+      const int v = slot_vector(tb.lim[j], tb.base[j], tl, wpr_log2, s.sub_lanes_log2, s.slice_vec, s.lay_k);
       off[j] = v >= 0 ? static_cast<uint32_t>(v) * 16u : kOutside;
     }
   }
@@ -412,58 +412,26 @@ __device__ __forceinline__ void head_sums(float (&q)[V], int hl, int lane) {
   }
 }
 
-// Grouped layout: slice k of the row is the aligned group of 2^gl lanes
-// holding vectors k 2^gl ... (k+1) 2^gl - 1 in one slot of one wavefront:
-// slot j, wavefront w of the team, group g give slice
-// k = (j wpr + w) 2^(6-gl) + g. Group sums come from the same butterfly as
-// the headwise form, read from each group's first lane (groups of 32 add
-// two 16-lane row sums); then the slices are added in ascending k, through
-// LDS when the team has several wavefronts.
-template <class E, int VPL>
-__device__ __forceinline__ float grouped_stat(const u32x4 (&d)[VPL], const Hot& s, const Layout<VPL>& L,
-                                              int wave, int lane, float* part, bool reuse) {
-  float q[VPL];
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) q[j] = E::sumsq(d[j], 0.f);
-  const int gl = s.group_log2;
-  head_sums<VPL>(q, gl < 4 ? gl : 4, lane);  // groups of up to 16 lanes
-  const int sv = 1 << gl;
-  const int ng = 64 >> gl;  // groups (slices) per wavefront slot
-  const int wi = wave & (L.wpr - 1);
-  float S = 0.f;
-  const int w0 = L.team << L.wpr_log2;
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) {
-    const int k0 = ((j << L.wpr_log2) + wi) * ng;  // first slice of this wavefront's slot j
-    for (int g = 0; g < ng; ++g) {
-      const float P = gl == 5 ? lane_value(q[j], g * 32) + lane_value(q[j], g * 32 + 16)
-                              : lane_value(q[j], g * sv);
-      if (L.wpr == 1)
-        S += P;  // slot-major, group-minor: ascending k
-      else if (lane == 0 && k0 + g < s.lay_k)
-        part[w0 * kWave + k0 + g] = P;
-    }
-  }
-  if (L.wpr > 1) {
-    __syncthreads();
-    const float Pk = lane < s.lay_k ? part[w0 * kWave + lane] : 0.f;
-    for (int k = 0; k < s.lay_k; ++k) S += lane_value(Pk, k);
-    if (reuse) __syncthreads();  // `part` is free again
-  }
-  return S;
-}
-
 // The row statistic S = sum over slices (ascending) of each slice's sum of
 // squares. Teams of several wavefronts add their partials through `part`
 // (one barrier, and a second one only when `reuse`: the workgroup goes on to
 // combine another row there; uniform over the workgroup); every lane of the
 // team returns the same S.
-template <class E, int VPL, bool MASKED>
+//
+// NARROW: the kernels for launches with slices narrower than a wavefront.
+// Their segments may have sub-teams of fewer than 64 lanes, sub-teams of
+// whole wavefronts, or the masked layout (told apart at run time); the
+// other kernels only see sub-teams of whole wavefronts.
+template <class E, int VPL, bool NARROW>
 __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, const Layout<VPL>& L,
                                           int wave, int lane, float* part, bool reuse) {
   float S = 0.f;
-  if constexpr (!MASKED) {
+  const int w0 = L.team << L.wpr_log2;
+  const bool narrow_subs = NARROW && s.sub_lanes_log2 < 6;
+  const bool masked = NARROW && s.masked;
+  if (!narrow_subs && !masked) {
     // slots are grouped by slice; a set bit in flush_mask closes a slice
+    // (this wavefront's share of it)
     float p = 0.f;
     int slice = 0;
 #pragma unroll
@@ -479,8 +447,36 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
         ++slice;
       }
     }
+  } else if (narrow_subs) {
+    // 2^(6-sl) sub-teams per wavefront. A set bit in flush_mask closes a
+    // round: every sub-team's current slice (sub-team u's round-i slice is
+    // u + i nsub). Group sums over each sub-team's lanes, read from its first
+    // lane, are whole slice partials.
+    const int sl = s.sub_lanes_log2;
+    const int nsw_log2 = 6 - sl;
+    float p = 0.f;
+    int round = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      p = E::sumsq(d[j], p);
+      if ((s.flush_mask >> j) & 1u) {
+        float g[1] = {p};
+        head_sums<1>(g, sl, lane);
+        const int k0 = ((wave & (L.wpr - 1)) << nsw_log2) + (round << (nsw_log2 + L.wpr_log2));
+        for (int u = 0; u < (1 << nsw_log2); ++u) {
+          const float P = lane_value(g[0], u << sl);
+          if (k0 + u < s.lay_k) {
+            if (L.wpr == 1)
+              S += P;  // round-major, sub-team-minor: ascending k
+            else if (lane == 0)
+              part[w0 * kWave + k0 + u] = P;
+          }
+        }
+        p = 0.f;
+        ++round;
+      }
+    }
   } else {
-    if (s.grouped) return grouped_stat<E, VPL>(d, s, L, wave, lane, part, reuse);
     // plain strided slots; each vector's squares join the partial of the
     // slice its index falls in
     float q[VPL];
@@ -502,18 +498,24 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
     }
   }
   if (L.wpr > 1) {
-    // slice k's partials come from the wavefronts of sub-team k % nsub, at
-    // index k / nsub of their partial lists; lane k gathers them (one LDS
-    // round trip for all lanes), then the slices are added in ascending k
+    // Sub-teams of whole wavefronts: slice k's partials come from the
+    // wavefronts of sub-team k % nsub, at index k / nsub of their partial
+    // lists. Narrower sub-teams wrote whole slice partials at index k of the
+    // team's first list. Lane k gathers slice k (one LDS round trip for all
+    // lanes), then the slices are added in ascending k.
     __syncthreads();
-    const int w0 = L.team << L.wpr_log2;
-    const int sub_log2 = MASKED ? L.wpr_log2 : s.sub_log2;
-    const int nsub_log2 = L.wpr_log2 - sub_log2;
     float Pk = 0.f;
     if (lane < s.lay_k) {
-      const int w1 = w0 + ((lane & ((1 << nsub_log2) - 1)) << sub_log2);
-      const int i = lane >> nsub_log2;
-      for (int w = 0; w < (1 << sub_log2); ++w) Pk += part[(w1 + w) * kWave + i];
+      if (!narrow_subs) {
+        // log2 of the wavefronts per sub-team (the whole team when masked)
+        const int sub_w = s.sub_lanes_log2 - 6;
+        const int nsub_log2 = L.wpr_log2 - sub_w;
+        const int w1 = w0 + ((lane & ((1 << nsub_log2) - 1)) << sub_w);
+        const int i = lane >> nsub_log2;
+        for (int w = 0; w < (1 << sub_w); ++w) Pk += part[(w1 + w) * kWave + i];
+      } else {
+        Pk = part[w0 * kWave + lane];
+      }
     }
     for (int k = 0; k < s.lay_k; ++k) S += lane_value(Pk, k);
     if (reuse) __syncthreads();  // `part` is free again
@@ -588,7 +590,7 @@ __device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const typenam
 
 // Finish one row whose data (and weights) are in registers: statistic (or
 // the precomputed partials), then scale and store, or publish the statistic.
-template <class E, int VPL, int MODE, bool MASKED, bool NT, bool CHECK = E::kSaturates>
+template <class E, int VPL, int MODE, bool NARROW, bool NT, bool CHECK = E::kSaturates>
 __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], const Hot& s,
                                            const Layout<VPL>& L, int64_t row, bool live, int wave,
                                            int lane, float* part, bool reuse) {
@@ -599,7 +601,7 @@ __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename
     if (live && lane < s.comb_k) pk = s.stats_in[static_cast<int64_t>(lane) * s.T + row];
     for (int k = 0; k < s.comb_k; ++k) S += lane_value(pk, k);
   } else {
-    S = row_stat<E, VPL, MASKED>(d, s, L, wave, lane, part, reuse);
+    S = row_stat<E, VPL, NARROW>(d, s, L, wave, lane, part, reuse);
   }
   if constexpr (MODE == MODE_STATS) {
     if (live && L.tl == 0) s.stats_out[row] = s.emit_rinv ? inv_rms(S, s.h, s.eps) : S;
@@ -670,7 +672,7 @@ __device__ __forceinline__ void gamma_from_lds(typename E::G (&g)[VPL], const La
 // stored, so reads of later rows overlap writes of earlier ones; gamma is
 // loaded once. Every wavefront of a workgroup runs the same number of
 // iterations (rows past T are empty), so barriers stay in step.
-template <class E, int VPL, bool MASKED, bool NT>
+template <class E, int VPL, bool NARROW, bool NT>
 __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L,
                                               int wave, int lane, float* part) {
   const int G = gridDim.x;
@@ -685,13 +687,13 @@ __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L
     const int g1 = g0 + G;
     const int64_t rb = static_cast<int64_t>(g1) * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(B, row_rsrc<E>(s.x, s.x_stride, rb, g1 < s.nwg && rb < s.T, s.row_bytes), L);
-    float S = row_stat<E, VPL, MASKED>(A, s, L, wave, lane, part, true);
+    float S = row_stat<E, VPL, NARROW>(A, s, L, wave, lane, part, true);
     scale_store<E, VPL, NT>(A, g, S, s, ra, ra < s.T, L);
     if (g1 >= s.nwg) break;
     const int g2 = g1 + G;
     ra = static_cast<int64_t>(g2) * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(A, row_rsrc<E>(s.x, s.x_stride, ra, g2 < s.nwg && ra < s.T, s.row_bytes), L);
-    S = row_stat<E, VPL, MASKED>(B, s, L, wave, lane, part, true);
+    S = row_stat<E, VPL, NARROW>(B, s, L, wave, lane, part, true);
     scale_store<E, VPL, NT>(B, g, S, s, rb, rb < s.T, L);
     if (g2 >= s.nwg) break;
     g0 = g2;
@@ -747,12 +749,12 @@ __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int 
   }
 }
 
-template <class E, int V, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE, int RPW>
+template <class E, int V, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW>
 __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wave, int lane, float* part,
                                      u32x4* lds_g) {
   const Layout<V> L(tb, s, wave, lane);
   if constexpr (RPW > 1) {
-    static_assert(!MASKED && !PIPE && MODE != MODE_HEAD, "several rows per wavefront: plain layouts only");
+    static_assert(!NARROW && !PIPE && MODE != MODE_HEAD, "several rows per wavefront: wavefront sub-teams only");
     body_rows<E, V, NW, MODE, NT, RPW>(s, L, wave, lane, part, lds_g);
   } else if constexpr (MODE == MODE_HEAD) {
     int gi = blockIdx.x;
@@ -769,7 +771,7 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
       head_finish<E, V, NT>(d2, g, s, L, row, row < s.T, lane);
     }
   } else if constexpr (PIPE) {
-    fwd_pipelined<E, V, MASKED, NT>(s, L, wave, lane, part);
+    fwd_pipelined<E, V, NARROW, NT>(s, L, wave, lane, part);
   } else {
     // The first group needs no bounds check (a group past the end holds only
     // empty rows), so its loads follow the argument loads directly.
@@ -787,7 +789,7 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
       else
         load_gamma<E, V>(g, s, L);
     }
-    row_finish<E, V, MODE, MASKED, NT>(d, g, s, L, row, live, wave, lane, part,
+    row_finish<E, V, MODE, NARROW, NT>(d, g, s, L, row, live, wave, lane, part,
                                        gi + static_cast<int>(gridDim.x) < s.nwg);
     // Only grids capped at the hardware limit get here. Reloading gamma each
     // time keeps the first row's registers free of this loop (holding them
@@ -799,7 +801,7 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
       typename E::G g2[V];
       load_row<E, V, NT>(d2, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
       if constexpr (MODE != MODE_STATS) load_gamma<E, V>(g2, s, L);
-      row_finish<E, V, MODE, MASKED, NT>(d2, g2, s, L, row, live, wave, lane, part,
+      row_finish<E, V, MODE, NARROW, NT>(d2, g2, s, L, row, live, wave, lane, part,
                                          gi + static_cast<int>(gridDim.x) < s.nwg);
     }
   }
@@ -809,21 +811,21 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
 // a narrower segment (the key rows of a grouped-query layout) runs the body
 // for VPL/2, VPL/4, ... slots instead, chosen by one uniform branch, so it
 // issues no instructions for slots it does not have.
-template <class E, int V, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE, int RPW>
+template <class E, int V, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW>
 __device__ __forceinline__ void dispatch(const Hot& s, const Tables<VPL>& tb, int wave, int lane,
                                          float* part, u32x4* lds_g) {
   if constexpr (V > 1) {
     if (s.nslot <= V / 2) {
-      dispatch<E, V / 2, VPL, NW, MODE, MASKED, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
+      dispatch<E, V / 2, VPL, NW, MODE, NARROW, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
       return;
     }
   }
-  body<E, V, VPL, NW, MODE, MASKED, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
+  body<E, V, VPL, NW, MODE, NARROW, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
 }
 
 // blockIdx.y selects the segment (query rows, key rows), so everything a
 // wavefront needs from the kernel arguments is one round of scalar loads.
-template <class E, int VPL, int NW, int MODE, bool MASKED, bool NT, bool PIPE, int RPW = 1>
+template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW = 1>
 __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   __shared__ float part[NW * kWave];  // per-wavefront slice partials (teams of > 1 wave)
   extern __shared__ u32x4 lds_g[];    // staged gamma (dynamic size: the launch's widest row)
@@ -832,7 +834,7 @@ __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   const Seg& seg = a.seg[blockIdx.y];
   const Hot s(a, seg);
   const Tables<VPL> tb(seg);
-  dispatch<E, VPL, VPL, NW, MODE, MASKED, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
+  dispatch<E, VPL, VPL, NW, MODE, NARROW, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
 }
 
 // Several rows per wavefront, 4-wavefront workgroups: statistics-only
@@ -868,7 +870,7 @@ hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hi
   if (v.mode == MODE_FWD) {
     if constexpr (NW == 4) {
       if (v.pipe) {
-        if (v.masked)
+        if (v.narrow)
           hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, true>), gd, bd, lds, st, a);
         else if (v.nt)
           hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, true>), gd, bd, lds, st, a);
@@ -877,7 +879,7 @@ hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hi
         return hipGetLastError();
       }
     }
-    if (v.masked)
+    if (v.narrow)
       hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, false>), gd, bd, lds, st, a);
     else if (v.nt)
       hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, false>), gd, bd, lds, st, a);
@@ -886,7 +888,7 @@ hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hi
   } else if (v.mode == MODE_HEAD) {
     hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_HEAD, false, true, false>), gd, bd, lds, st, a);
   } else if (v.mode == MODE_STATS) {
-    if (v.masked)
+    if (v.narrow)
       hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, true, true, false>), gd, bd, lds, st, a);
     else
       hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, false, true, false>), gd, bd, lds, st, a);

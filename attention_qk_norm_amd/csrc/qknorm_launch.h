@@ -5,19 +5,21 @@
 // is processed by teams of `wpr` wavefronts; a team owns one row at a time.
 //
 // Register layout of a row inside a team ("slots"): the row's 16-byte
-// vectors are grouped by column slice, and each slice's vectors are dealt to
-// the team's lanes starting again at lane 0 of the team. Slot j of a lane
-// therefore always lies inside one slice, and a slice's partial sum of squares
-// is a plain team-wide reduction over the slots of that slice. `sps` slots
-// cover one slice; a row needs `lay_k * sps` slots per lane. With one slice
-// this is the usual strided layout (vector v in lane v % team, slot v / team).
+// vectors are grouped by column slice. The team's lanes form sub-teams of
+// 2^sub_lanes_log2 lanes (a power of two from one lane to the whole team);
+// sub-team u takes slices u, u + nsub, u + 2 nsub, ... one after the other
+// and deals each slice's vectors over its own lanes from its lane 0. Slot j
+// of a lane therefore always lies inside one slice, and a slice's partial sum
+// of squares is a reduction over its sub-team's lanes and the slots of that
+// slice. With one slice and sub-teams as wide as the team this is the usual
+// strided layout (vector v in lane v % team, slot v / team). Sub-teams
+// narrower than a wavefront serve many narrow slices: with as many sub-teams
+// as slices, each lane holds one slice in all its slots, and a group sum over
+// the sub-team's lanes gives the partial.
 //
-// When that would need too many slots (many slices narrower than the team),
-// the kernel falls back to the "masked" layout: plain strided vectors, and a
-// per-lane slice index selects which partial each vector's squares join.
-// When a slice is a power of two of at most 32 vectors, the strided layout
-// puts each slice in one aligned group of lanes of one slot ("grouped"), and
-// the partials come from group sums instead of per-lane masks.
+// When every such layout would need too many slots, the kernel falls back to
+// the "masked" layout: plain strided vectors, and a per-lane slice index
+// selects which partial each vector's squares join.
 //
 // Headwise rows use the one-slice (strided) layout. A head is a power of two
 // of at most 64 vectors, so each head sits in one slot of one aligned group
@@ -45,6 +47,7 @@ constexpr int kMaxSlots = 16;  // slots per lane of the widest compiled variant
 // row; slot_lim[j] packs the lanes it covers (low 16 bits) and which of the
 // sub-team's slices it belongs to (high 16 bits). Sub-team u adds
 // u * slice_vec to the base and owns slices u, u + nsub, u + 2 nsub, ...
+// (nsub = team lanes / sub-team lanes).
 struct Seg {
   const void* x;          // row 0 of the input
   void* y;                // row 0 of the output (FWD, APPLY, HEAD)
@@ -54,7 +57,7 @@ struct Seg {
   int64_t x_stride;       // elements between input rows
   int64_t y_stride;       // elements between output rows
   int32_t wpr_log2;       // log2 of the wavefronts per team
-  int32_t sub_log2;       // log2 of the wavefronts per sub-team (deals one slice)
+  int32_t sub_lanes_log2; // log2 of the lanes per sub-team (deals one slice at a time)
   int32_t lds_gamma;      // 1: the workgroup stages gamma in LDS and its rows share it
   int32_t rows_per_wg;    // teams per workgroup
   int32_t nwg;            // workgroups covering all T rows
@@ -62,6 +65,7 @@ struct Seg {
   uint32_t row_bytes;     // bytes of one row processed (and of its weights)
   int32_t lay_k;          // partial sums per row (slices)
   int32_t comb_k;         // APPLY: partials combined per row
+  int32_t masked;         // masked layout (kernels for narrow slices only)
   int32_t slice_vec;      // masked layout: vectors per slice
   float inv_slice_vec;    // masked layout: 1.0f / slice_vec
   float h;                // the mean of squares divides by this width
@@ -69,8 +73,6 @@ struct Seg {
   int32_t head_log2;      // HEAD: log2 of the 16-byte vectors per head (0 ... 6)
   float inv_h;            // HEAD: 1 / head width (a power of two, so exact)
   int32_t emit_rinv;      // STATS: write 1 / sqrt(S / h + eps) instead of S
-  int32_t grouped;        // masked layout whose slices are aligned lane groups of
-  int32_t group_log2;     //   2^group_log2 (<= 32) vectors: group sums, no masks
   int32_t rpw;            // rows each one-wavefront team takes at once (1, 2, 4)
   int32_t slot_base[kMaxSlots];
   int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
@@ -85,11 +87,11 @@ struct Args {
 // The row vector that slot j of team lane `tl` holds, or -1 when the slot is
 // empty there. `lim_word` and `base` are the slot's table entries. Used by
 // the kernels and by the host-side layout checks.
-__host__ __device__ inline int slot_vector(int lim_word, int base, int tl, int wpr_log2, int sub_log2,
+__host__ __device__ inline int slot_vector(int lim_word, int base, int tl, int wpr_log2, int sub_lanes_log2,
                                            int slice_vec, int K) {
-  const int sub = (tl >> 6) >> sub_log2;         // sub-team within the team
-  const int stl = tl & ((64 << sub_log2) - 1);  // lane within the sub-team
-  const int slice = sub + ((lim_word >> 16) << (wpr_log2 - sub_log2));
+  const int sub = tl >> sub_lanes_log2;             // sub-team within the team
+  const int stl = tl & ((1 << sub_lanes_log2) - 1);  // lane within the sub-team
+  const int slice = sub + ((lim_word >> 16) << (6 + wpr_log2 - sub_lanes_log2));
   return (stl < (lim_word & 0xffff) && slice < K) ? base + sub * slice_vec + stl : -1;
 }
 
@@ -99,7 +101,8 @@ struct Variant {
   int mode;      // Mode
   int vpl;       // slots per lane the kernel is built for (>= what the segments need)
   int nw;        // wavefronts per workgroup: 4 or 16
-  bool masked;   // FWD, STATS: masked layout
+  bool narrow;   // FWD, STATS: slices narrower than a wavefront (sub-teams of
+                 // fewer than 64 lanes, or the masked layout)
   bool nt;       // FWD only: non-temporal row loads and stores
   bool pipe;     // FWD only: persistent workgroups with the next rows prefetched
   int rpw = 1;   // rows per one-wavefront team (1, or 2 / 4 for rows of at most 2 slots)

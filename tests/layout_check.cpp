@@ -33,6 +33,7 @@ hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes
 }  // namespace qkn
 
 static int failures = 0;
+static long g_layouts[3];  // segments laid out with whole-wavefront sub-teams, narrower ones, masked
 #define CHECK(c, ...)                          \
   do {                                         \
     if (!(c)) {                                \
@@ -52,19 +53,20 @@ static int body_slots(int vpl, int nslot) {  // the kernel's dispatch: VPL, VPL/
 }
 
 static void check_seg(const qkn::Seg& s, int nw, int vpl, int64_t nvec, int K, bool masked, const char* what) {
-  const int wl = s.wpr_log2, m = s.sub_log2;
-  CHECK(m >= 0 && m <= wl, "%s sub_log2 %d wpr_log2 %d", what, m, wl);
+  const int wl = s.wpr_log2, m = s.sub_lanes_log2;
+  CHECK(m >= 0 && m <= 6 + wl, "%s sub_lanes_log2 %d wpr_log2 %d", what, m, wl);
+  CHECK(!masked || m == 6 + wl, "%s masked layout with sub-teams of 2^%d lanes", what, m);
   CHECK(s.nslot >= 1 && s.nslot <= vpl, "%s nslot %d vpl %d", what, s.nslot, vpl);
   CHECK(s.rows_per_wg * (1 << wl) == nw, "%s rows_per_wg", what);
   CHECK(static_cast<int64_t>(s.row_bytes) == nvec * 16, "%s row_bytes", what);
   const int lanes = 64 << wl;
-  const int nsub = 1 << (wl - m);
+  const int nsub = 1 << (6 + wl - m);
   const int64_t sv = s.slice_vec;
   std::vector<int> count(nvec, 0);
   // slice held by (sub-team, slot); -2 = unset, -1 = empty for this sub-team
   std::vector<std::vector<int>> slot_slice(nsub, std::vector<int>(s.nslot, -2));
   for (int tl = 0; tl < lanes; ++tl) {
-    const int sub = (tl >> 6) >> m;
+    const int sub = tl >> m;
     for (int j = 0; j < s.nslot; ++j) {
       const int v = qkn::slot_vector(s.slot_lim[j], s.slot_base[j], tl, wl, m, s.slice_vec, s.lay_k);
       if (v < 0) continue;
@@ -121,26 +123,33 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
           (long long)hk, K);
     return;
   }
-  bool masked = false;
-  for (int i = 0; i < nseg; ++i) masked = masked || plans[i].masked;
+  bool narrow = false;
+  for (int i = 0; i < nseg; ++i) narrow = narrow || narrow_plan(plans[i]);
   int slots = 0;
   qkn::Seg seg[2];
-  for (int i = 0; i < nseg; ++i) {
-    Plan pl = plans[i];
-    if (masked && !pl.masked) pl = Plan{pl.wpr_log2, pl.wpr_log2, plain_slots(in[i].nvec, pl.wpr_log2), true};
-    fill_layout(&seg[i], pl, nw, in[i].nvec, K, T);
-    share_gamma(&seg[i], dtype);
-    slots = seg[i].nslot > slots ? seg[i].nslot : slots;
-  }
-  const int vpl = qkn::compiled_vpl(slots, nw, dtype);
+  bool masked[2] = {false, false};
   char what[160];
   std::snprintf(what, sizeof what, "T=%lld hq=%lld hk=%lld K=%d wpr=%d dt=%d", (long long)T, (long long)hq,
                 (long long)hk, K, forced_wpr, dtype);
+  for (int i = 0; i < nseg; ++i) {
+    masked[i] = plans[i].masked;
+    fill_layout(&seg[i], plans[i], nw, in[i].nvec, K, T);
+    share_gamma(&seg[i], dtype);
+    slots = seg[i].nslot > slots ? seg[i].nslot : slots;
+    // the kernels for narrow slices tell the layouts apart by the masked
+    // flag and the sub-team width; the others only ever see sub-teams of
+    // whole wavefronts
+    const int sl = seg[i].sub_lanes_log2;
+    CHECK(seg[i].masked == (masked[i] ? 1 : 0), "%s seg %d masked flag", what, i);
+    CHECK(!masked[i] || sl == 6 + seg[i].wpr_log2, "%s seg %d masked with sub-teams 2^%d", what, i, sl);
+    CHECK(narrow || (!masked[i] && sl >= 6), "%s wavefront kernel, seg %d: sub-teams 2^%d", what, i, sl);
+  }
+  const int vpl = qkn::compiled_vpl(slots, nw, dtype);
   CHECK(vpl > 0, "%s no compiled variant for %d slots", what, slots);
   if (vpl == 0) return;
   // several rows per wavefront: every row covered once, no spare workgroups
   for (int mode : {qkn::MODE_STATS, qkn::MODE_FWD}) {
-    qkn::Variant v{dtype, mode, vpl, nw, masked, true, false};
+    qkn::Variant v{dtype, mode, vpl, nw, narrow, true, false};
     qkn::Args a{};
     a.T = T;
     for (int i = 0; i < nseg; ++i) a.seg[i] = seg[i];
@@ -150,19 +159,15 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
       CHECK(a.seg[i].rpw == v.rpw && (v.rpw == 1 || v.rpw == 2 || v.rpw == 4), "%s rpw %d", what, v.rpw);
       CHECK(int64_t{a.seg[i].nwg} * per_wg >= T && int64_t{a.seg[i].nwg - 1} * per_wg < T, "%s nwg %d", what,
             a.seg[i].nwg);
-      CHECK(v.rpw == 1 || (a.seg[i].wpr_log2 == 0 && !masked && nw == 4 &&
+      CHECK(v.rpw == 1 || (a.seg[i].wpr_log2 == 0 && !narrow && nw == 4 &&
                            (mode == qkn::MODE_STATS ? a.seg[i].nslot * v.rpw <= 4
                                                     : dtype == QKNORM_FP8_E4M3 && v.rpw == 2 && a.seg[i].nslot <= 8)),
             "%s mode %d rpw %d with wpr_log2 %d, %d slots", what, mode, v.rpw, a.seg[i].wpr_log2, a.seg[i].nslot);
     }
   }
   for (int i = 0; i < nseg; ++i) {
-    check_seg(seg[i], nw, vpl, in[i].nvec, K, masked, what);
-    // grouped: every slice is one aligned lane group of one slot, in order
-    if (masked && seg[i].grouped) {
-      CHECK((int64_t{1} << seg[i].group_log2) * K == in[i].nvec, "%s group size", what);
-      check_heads(seg[i], 1 << seg[i].group_log2, what);
-    }
+    check_seg(seg[i], nw, vpl, in[i].nvec, K, masked[i], what);
+    ++g_layouts[masked[i] ? 2 : seg[i].sub_lanes_log2 < 6 ? 1 : 0];
   }
 }
 
@@ -170,7 +175,7 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
 // slot, either nothing or the hv vectors of one head in order, so lane l
 // holds the head's vector l mod hv (the kernel's head sum and weights).
 static void check_heads(const qkn::Seg& s, int hv, const char* what) {
-  const int wl = s.wpr_log2, m = s.sub_log2, lanes = 64 << wl;
+  const int wl = s.wpr_log2, m = s.sub_lanes_log2, lanes = 64 << wl;
   for (int j = 0; j < s.nslot; ++j)
     for (int g0 = 0; g0 < lanes; g0 += hv) {
       const int v0 = qkn::slot_vector(s.slot_lim[j], s.slot_base[j], g0, wl, m, s.slice_vec, 1);
@@ -206,7 +211,7 @@ static void run_headwise(int64_t T, int64_t hq, int64_t hk, int64_t D, int force
   qkn::Seg seg[2];
   int slots = 0;
   for (int i = 0; i < nseg; ++i) {
-    CHECK(!plans[i].masked, "%s masked plan", what);
+    CHECK(!narrow_plan(plans[i]), "%s narrow plan", what);
     fill_layout(&seg[i], plans[i], nw, in[i].nvec, 1, T);
     slots = seg[i].nslot > slots ? seg[i].nslot : slots;
   }
@@ -254,6 +259,8 @@ int main() {
             cases += 2;
           }
       }
+  std::printf("segments: %ld whole-wavefront sub-teams, %ld narrower sub-teams, %ld masked\n", g_layouts[0],
+              g_layouts[1], g_layouts[2]);
   std::printf("%d cases, %d failures\n", cases, failures);
   return failures ? 1 : 0;
 }

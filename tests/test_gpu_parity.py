@@ -192,14 +192,15 @@ RAGGED = [
     # (dtype, T, Hq, Hk, K)
     ("bf16", 1, 8, 8, 1),
     ("bf16", 3, 24, 16, 1),
-    ("bf16", 5, 1000, 200, 5),       # ragged last slot, slices of 200 / 40
+    ("bf16", 5, 1000, 200, 5),       # slices of 25 / 5 vectors: 32- and 8-lane sub-teams over 4 wavefronts
     ("bf16", 63, 1032, 520, 1),
     ("bf16", 65, 5120, 1024, 4),     # C3/C4 widths, odd T
-    ("bf16", 7, 4096, 4096, 64),     # 64 slices of 8 vectors: grouped layout
-    ("bf16", 7, 1536, 1536, 64),     # slices of 3 vectors: masked layout
-    ("bf16", 11, 2048, 512, 32),     # groups of 8 and 2 vectors
-    ("bf16", 5000, 1024, 1024, 8),   # groups of 16, two wavefronts per row (LDS combine)
-    ("f32", 9, 4096, 256, 64),       # groups of 16 and of 1 vector
+    ("bf16", 7, 4096, 4096, 64),     # 64 slices of 8 vectors: 4-lane sub-teams, LDS combine
+    ("bf16", 7, 1536, 1536, 64),     # slices of 3 vectors: ragged 4-lane sub-teams
+    ("bf16", 11, 2048, 512, 32),     # 8- and 2-lane sub-teams
+    ("bf16", 5000, 1024, 1024, 8),   # 8-lane sub-teams, one wavefront per row
+    ("bf16", 2048, 3072, 3072, 48),  # 4-lane sub-teams taking 3 slices each in turn
+    ("f32", 9, 4096, 256, 64),       # 4-lane and 1-lane sub-teams
     ("bf16", 9, 12288, 1536, 3),
     ("bf16", 4, 16384, 16384, 8),    # wider than one wavefront's 16 slots
     ("bf16", 3, 65536, 8, 1),        # widest accepted row, with a tiny key row
@@ -210,8 +211,10 @@ RAGGED = [
     ("f32", 17, 4096, 1024, 2),
     ("f32", 3, 8192, 8192, 8),
     ("f32", 2, 32768, 4, 1),         # widest fp32 row
-    ("f32", 5, 1536, 1536, 48),      # 48 slices of 8 vectors: grouped layout
-    ("f32", 5, 1920, 1920, 40),      # slices of 12 vectors: masked layout
+    ("f32", 5, 1536, 1536, 48),      # 48 slices of 8 vectors: 4-lane sub-teams
+    ("f32", 5, 1920, 1920, 40),      # slices of 12 vectors: ragged 4-lane sub-teams
+    ("f32", 2048, 200, 200, 5),      # slices of 10 vectors: masked layout, one wavefront per row
+    ("f32", 3, 200, 40, 10),         # masked layout over 4 wavefronts (LDS combine)
 ]
 
 
