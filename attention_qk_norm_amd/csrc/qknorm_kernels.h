@@ -10,8 +10,9 @@
 //      row stays resident, so HBM is read once);
 //   2. per slice, each lane accumulates its slots' squares in fp32; a
 //      wavefront reduction (DPP within rows of 16 lanes, then 4 readlanes)
-//      gives the slice's partial; teams of several wavefronts add their
-//      partials through LDS;
+//      gives the slice's partial, or, for slices narrower than a wavefront,
+//      a sum over the slice's aligned group of lanes; teams of several
+//      wavefronts add their partials through LDS;
 //   3. the partials are summed in ascending slice order (review Eq. 5), then
 //      r = 1 / sqrt(S / H + eps) with H the full width (Eq. 6);
 //   4. y = (x * r) * gamma (Eq. 1 order), rounded to the output type, stored
@@ -89,6 +90,8 @@ struct F32 : SameTypeGamma {
     }
     return acc;
   }
+  // fp32 and bf16 results cannot leave their type's range here, so SAT and
+  // the running maximum (for types that saturate) are unused
   static constexpr bool kSaturates = false;
   template <bool SAT>
   static __device__ __forceinline__ u32x4 encode(u32x4 d, u32x4 g, float r, float&) {
@@ -374,9 +377,9 @@ __device__ __forceinline__ void load_gamma(typename E::G (&g)[VPL], const Hot& s
   for (int j = 0; j < VPL; ++j) g[j] = E::load_gamma(r, L.off[j]);
 }
 
-// Headwise (review, "Layerwise vs. headwise QK-Norm"): sums over aligned
-// groups of 2^hl lanes (hl <= 6), one group per head, every lane of a group
-// receiving the same value. Within a row of 16 lanes each butterfly step
+// Sums over aligned groups of 2^hl lanes (hl <= 6), every lane of a group
+// receiving the same value: the heads of the headwise form (review,
+// "Layerwise vs. headwise QK-Norm"), and the slices of narrow sub-teams. Within a row of 16 lanes each butterfly step
 // adds the partner group's sum, and the addition is commutative, so the
 // lanes agree bit for bit; groups of 32 and 64 lanes add the row sums read
 // from lanes 0, 16, 32 and 48 in a fixed order.
