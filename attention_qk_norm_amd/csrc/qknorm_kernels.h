@@ -465,14 +465,16 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
       if ((s.flush_mask >> j) & 1u) {
         float g[1] = {p};
         head_sums<1>(g, sl, lane);
+        // this wavefront's sub-teams hold slices k0, k0 + 1, ... this round
         const int k0 = ((wave & (L.wpr - 1)) << nsw_log2) + (round << (nsw_log2 + L.wpr_log2));
-        for (int u = 0; u < (1 << nsw_log2); ++u) {
-          const float P = lane_value(g[0], u << sl);
-          if (k0 + u < s.lay_k) {
-            if (L.wpr == 1)
-              S += P;  // round-major, sub-team-minor: ascending k
-            else if (lane == 0)
-              part[w0 * kWave + k0 + u] = P;
+        const int last = min(k0 + (1 << nsw_log2), s.lay_k);
+        if (L.wpr == 1) {
+          // round-major, sub-team-minor: ascending k
+          for (int k = k0, l = 0; k < last; ++k, l += 1 << sl) S += lane_value(g[0], l);
+        } else {
+          for (int k = k0, l = 0; k < last; ++k, l += 1 << sl) {
+            const float P = lane_value(g[0], l);
+            if (lane == 0) part[w0 * kWave + k] = P;
           }
         }
         p = 0.f;
