@@ -517,7 +517,18 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
         const int nsub_log2 = L.wpr_log2 - sub_w;
         const int w1 = w0 + ((lane & ((1 << nsub_log2) - 1)) << sub_w);
         const int i = lane >> nsub_log2;
-        for (int w = 0; w < (1 << sub_w); ++w) Pk += part[(w1 + w) * kWave + i];
+        // four reads in flight at a time, added in wavefront order; reads
+        // past the sub-team repeat its last wavefront and add zero (partials
+        // are sums of squares, never -0, so adding +0 changes nothing)
+        const int cnt = 1 << sub_w;
+        if (cnt == 1) Pk = part[w1 * kWave + i];
+        for (int w = 0; cnt > 1 && w < cnt; w += 4) {
+          float x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] = part[(w1 + min(w + u, cnt - 1)) * kWave + i];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) Pk += w + u < cnt ? x[u] : 0.f;
+        }
       } else {
         Pk = part[w0 * kWave + lane];
       }
