@@ -350,6 +350,15 @@ void fill_layout(qkn::Seg* s, const Plan& p, int nw, int64_t nvec, int K, int64_
   }
 }
 
+// The width the mean of squares divides by, and its reciprocal (rounded
+// once, from double): the kernels form the mean as S * (1/H), exact when H is
+// a power of two and otherwise within an ulp of S / H, which keeps a
+// division off the path from the statistic to the scaling.
+void set_width(qkn::Seg* s, int64_t h) {
+  s->h = static_cast<float>(h);
+  s->inv_h = static_cast<float>(1.0 / static_cast<double>(h));
+}
+
 // Bytes of the weights of one row of `row_bytes` bytes.
 uint32_t gamma_bytes(uint32_t row_bytes, int dtype) {
   return row_bytes / static_cast<uint32_t>(elem_bytes(dtype)) * static_cast<uint32_t>(gamma_elem_bytes(dtype));
@@ -523,7 +532,7 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
     // either needs them (they also run the other layouts)
     fill_layout(&s, plans[i], nw, in[i].nvec, num_slices, T);
     share_gamma(&s, dtype);
-    s.h = static_cast<float>(segs[i]->width);
+    set_width(&s, segs[i]->width);
     s.comb_k = 0;
     slots = s.nslot > slots ? s.nslot : slots;
   }
@@ -572,8 +581,7 @@ int qknorm_forward_headwise(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_
     s.y_stride = segs[i]->y_stride;
     fill_layout(&s, plans[i], nw, in[i].nvec, 1, T);
     s.head_log2 = hl;
-    s.h = static_cast<float>(head_dim);
-    s.inv_h = 1.0f / static_cast<float>(head_dim);
+    set_width(&s, head_dim);
     slots = s.nslot > slots ? s.nslot : slots;
   }
   qkn::Variant v{dtype, qkn::MODE_HEAD, qkn::compiled_vpl(slots, nw, dtype), nw, false, true, false};
@@ -629,7 +637,7 @@ int qknorm_inv_rms(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
     s.x_stride = segs[i]->x_stride;
     s.stats_out = outs[i];
     fill_layout(&s, plans[i], nw, in[i].nvec, num_slices, T);
-    s.h = static_cast<float>(segs[i]->width);
+    set_width(&s, segs[i]->width);
     s.emit_rinv = 1;
     slots = s.nslot > slots ? s.nslot : slots;
   }
@@ -670,7 +678,7 @@ int qknorm_partial_stats(qknorm_ctx* ctx, int dtype, int64_t T, const void* x_sl
   s.x_stride = x_stride;
   s.stats_out = out;
   fill_layout(&s, plan, nw, nvec, 1, T);
-  s.h = static_cast<float>(slice_width);
+  set_width(&s, slice_width);
   qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(s.nslot, nw, dtype), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, 1, stream);
@@ -716,7 +724,7 @@ int qknorm_apply_stats(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows*
   fill_layout(&s, plan, nw, nvec, 1, T);
   share_gamma(&s, dtype);
   s.comb_k = num_slices;
-  s.h = static_cast<float>(h_total);
+  set_width(&s, h_total);
   qkn::Variant v{dtype, qkn::MODE_APPLY, qkn::compiled_vpl(s.nslot, nw, dtype), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
   return run(ctx, v, a, 1, stream);

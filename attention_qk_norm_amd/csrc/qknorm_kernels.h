@@ -550,8 +550,11 @@ __device__ __forceinline__ float rsqrt_full(float a) {
 
 // The inverse RMS of a row (review Eq. 6): the fused forward and the
 // statistic-only output use this same expression, so they agree bit for bit.
-__device__ __forceinline__ float inv_rms(float S, float h, float eps) {
-  return rsqrt_full(S / h + eps);
+// The mean is S times the host's 1/H (exact for a power-of-two H, otherwise
+// within an ulp of S / H) with eps added in the same fused multiply-add, so
+// no division sits between the statistic and the scaling.
+__device__ __forceinline__ float inv_rms(float S, float inv_h, float eps) {
+  return rsqrt_full(__builtin_fmaf(S, inv_h, eps));
 }
 
 // Scale and store a lane's vectors: vector j with weights gw(j) and inverse
@@ -596,7 +599,7 @@ __device__ __forceinline__ void encode_store(const u32x4 (&d)[VPL], GW gw, RW rw
 template <class E, int VPL, bool NT, bool CHECK = E::kSaturates>
 __device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], float S,
                                             const Hot& s, int64_t row, bool live, const Layout<VPL>& L) {
-  const float r = inv_rms(S, s.h, s.eps);
+  const float r = inv_rms(S, s.inv_h, s.eps);
   const auto grs = rsrc(s.gamma, s.row_bytes * E::kGammaScale);
   encode_store<E, VPL, NT, CHECK>(
       d, [&](int j) -> const typename E::G& { return g[j]; }, [&](int) { return r; },
@@ -620,7 +623,7 @@ __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename
     S = row_stat<E, VPL, NARROW>(d, s, L, wave, lane, part, reuse);
   }
   if constexpr (MODE == MODE_STATS) {
-    if (live && L.tl == 0) s.stats_out[row] = s.emit_rinv ? inv_rms(S, s.h, s.eps) : S;
+    if (live && L.tl == 0) s.stats_out[row] = s.emit_rinv ? inv_rms(S, s.inv_h, s.eps) : S;
   } else {
     scale_store<E, VPL, NT, CHECK>(d, g, S, s, row, live, L);
   }

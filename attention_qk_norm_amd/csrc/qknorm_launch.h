@@ -71,7 +71,7 @@ struct Seg {
   float h;                // the mean of squares divides by this width
   uint32_t flush_mask;    // segmented layout: bit j set when slot j ends a slice
   int32_t head_log2;      // HEAD: log2 of the 16-byte vectors per head (0 ... 6)
-  float inv_h;            // HEAD: 1 / head width (a power of two, so exact)
+  float inv_h;            // 1 / h, rounded once (exact for HEAD's power-of-two heads)
   int32_t emit_rinv;      // STATS: write 1 / sqrt(S / h + eps) instead of S
   int32_t rpw;            // rows each one-wavefront team takes at once (1, 2, 4)
   int32_t slot_base[kMaxSlots];
