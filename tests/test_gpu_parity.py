@@ -610,3 +610,47 @@ def test_denormal_statistics():
     assert_parity(r, ref, torch.float32, "rinv")
     assert_parity(y, oracle.forward(x, g, eps, 1)[0], torch.float32, "forward")
     assert_parity(yh, oracle.headwise(x, g[:D], D, eps), torch.float32, "headwise")
+
+
+@pytest.mark.parametrize("opts", [dict(max_workgroups=3), dict(max_workgroups=1, waves_per_row=2),
+                                  dict(max_workgroups=5, waves_per_row=16)],
+                         ids=lambda o: ",".join("%s=%s" % kv for kv in o.items()))
+def test_capped_grids_statistics_and_split_path(opts):
+    """Grids capped below the row count: the statistic-only, partial-sum and
+    apply launches loop over their rows (grid stride) and reproduce, bit for
+    bit, the same layout's results on a full grid (a different team size
+    would add the squares in another order); both match the oracle."""
+    ctx = qk.Context(0, **opts)
+    full = qk.Context(0, waves_per_row=opts.get("waves_per_row", 0))
+    T, Hq, Hk, K = 300, 4096, 1024, 4
+    q = workloads.random_rows(T, Hq, "bf16", [61, T], dist="laplace")
+    k = workloads.random_rows(T, Hk, "bf16", [62, T])
+    qd, kd = gpu(q), gpu(k)
+    say("capped inv_rms", opts)
+    a_q, a_k = qk.inv_rms(qd, kd, eps=1e-6, num_slices=K, ctx=full)
+    b_q, b_k = qk.inv_rms(qd, kd, eps=1e-6, num_slices=K, ctx=ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(a_q, b_q) and torch.equal(a_k, b_k)
+    for r, x, which in ((b_q, q, "q"), (b_k, k, "k")):
+        assert_parity(r, oracle.inv_rms(x, 1e-6, K), torch.float32, "capped rinv " + which)
+    w = Hq // K
+    P = oracle.slice_sumsq(q, K)
+    stats = {}
+    for name, c in (("default", full), ("capped", ctx)):
+        st = torch.zeros((K, T), dtype=torch.float32, device=DEV)
+        say("capped partial_stats", name, opts)
+        for s in range(K):
+            qk.partial_stats(qd[:, s * w:(s + 1) * w], s, K, st, ctx=c)
+        torch.cuda.synchronize()
+        stats[name] = st
+    assert torch.equal(stats["default"], stats["capped"])
+    np.testing.assert_allclose(stats["capped"].cpu().double().numpy(), P, rtol=2e-6)
+    g = gpu(workloads.random_weights(Hq, "bf16", 63))
+    for s in (0, K - 1):
+        say("capped apply_stats", s, opts)
+        ya = qk.apply_stats(qd[:, s * w:(s + 1) * w], g[s * w:(s + 1) * w], stats["default"], Hq, eps=1e-6,
+                            ctx=full)
+        yb = qk.apply_stats(qd[:, s * w:(s + 1) * w], g[s * w:(s + 1) * w], stats["default"], Hq, eps=1e-6,
+                            ctx=ctx)
+        torch.cuda.synchronize()
+        assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
