@@ -154,6 +154,14 @@ def random_rows(T, H, dtype, seed, dist="normal", scale=1.0):
     return _finish(a.reshape(T, H), dtype)
 
 
+def device_rows(T, H, dtype, seed, device):
+    """Seeded N(0,1) [T, H] rows drawn on the device (torch's generator), for
+    inputs too large to draw on the host; tests copy back the rows they check."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.randn((T, H), generator=g, device=device, dtype=torch.float32).to(DTYPES[dtype])
+
+
 def random_weights(H, dtype, seed, lo=0.5, hi=1.5):
     g = np.random.default_rng(seed).uniform(lo, hi, H).astype(np.float32)
     return _finish(g, dtype)

@@ -654,3 +654,28 @@ def test_capped_grids_statistics_and_split_path(opts):
                             ctx=ctx)
         torch.cuda.synchronize()
         assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
+
+
+def test_rows_beyond_the_grid_limit():
+    """More workgroups than one launch holds (2^32 - 1 work-items along x):
+    2^28 + 4096 one-vector bf16 rows (4.3 GB). The statistic-only launch (16
+    rows per workgroup) and the in-place forward (4) cover the rows past the
+    first grid with their grid-stride loops; sampled rows (the first, random
+    ones, and the last, which only the loop reaches) match the oracle."""
+    T, H = (1 << 28) + 4096, 8
+    say("rows beyond the grid limit: T=%d, width %d" % (T, H))
+    x = workloads.device_rows(T, H, "bf16", 71, DEV)
+    g = gpu(workloads.random_weights(H, "bf16", 72))
+    r, _ = qk.inv_rms(x, None, eps=1e-6)
+    rng = np.random.default_rng(73)
+    idx = torch.from_numpy(np.concatenate([np.arange(1000), rng.integers(0, T, 2000),
+                                           np.arange(T - 5000, T)])).to(DEV)
+    xs = x.index_select(0, idx).cpu()
+    rs = r.index_select(0, idx).cpu()
+    say("rows beyond the grid limit: forward in place")
+    qk.forward(x, None, g, None, eps=1e-6, out_q=x)
+    torch.cuda.synchronize()
+    ys = x.index_select(0, idx).cpu()
+    del x, r
+    assert_parity(rs, oracle.inv_rms(xs, 1e-6, 1), torch.float32, "rinv")
+    assert_parity(ys, oracle.forward(xs, g.cpu(), 1e-6, 1)[0], torch.bfloat16, "y")
