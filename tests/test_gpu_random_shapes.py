@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 VEC = {"f32": 4, "bf16": 8, "fp8": 16}
-N_CASES = 60
+N_CASES = int(os.environ.get("QKNORM_RANDOM_CASES", "60"))  # more for a longer sweep
 
 
 @pytest.fixture(scope="module", autouse=True)
