@@ -81,6 +81,15 @@ SHAPES = [
     (2, 65536, 16, 1),         # widest fp8 row
     (3000, 512, 128, 2),       # many rows per SIMD
     (2001, 5120, 1024, 1),     # one round of wavefronts, 2 rows each; ragged T
+    # FP8 bodies of odd slot counts: 3 slots (2 rows per wavefront); 7 slots
+    # with a 2-slot key segment (its 3-slot body keeps one slot empty); 5 and
+    # 3 slots over several rounds, sliced; 7 slots over several rounds; 7
+    # slots with widened teams
+    (1500, 3072, 1024, 1),
+    (1100, 7168, 2048, 1),
+    (9000, 5120, 3072, 8),
+    (12000, 7168, 1024, 1),
+    (40, 7168, 7168, 7),
 ]
 
 
