@@ -921,16 +921,15 @@ template <class E>
 hipError_t launch_dtype(const Variant& v, const Args& a, dim3 grid, unsigned lds, hipStream_t st) {
   // only the slot counts the element type may use are instantiated
   constexpr int kCap4 = max_slots(E::kDtype, 4), kCap16 = max_slots(E::kDtype, 16);
-  constexpr bool kFp8 = E::kDtype == QKNORM_FP8_E4M3;  // odd slot counts: FP8 only
   if (v.nw == 4) {
     switch (v.vpl) {
       case 1: return launch_vpl<E, 1, 4>(v, a, grid, lds, st);
       case 2: return launch_vpl<E, 2, 4>(v, a, grid, lds, st);
-      case 3: if constexpr (kFp8) return launch_vpl<E, 3, 4>(v, a, grid, lds, st); break;
+      case 3: return launch_vpl<E, 3, 4>(v, a, grid, lds, st);
       case 4: return launch_vpl<E, 4, 4>(v, a, grid, lds, st);
-      case 5: if constexpr (kFp8) return launch_vpl<E, 5, 4>(v, a, grid, lds, st); break;
+      case 5: return launch_vpl<E, 5, 4>(v, a, grid, lds, st);
       case 6: return launch_vpl<E, 6, 4>(v, a, grid, lds, st);
-      case 7: if constexpr (kFp8) return launch_vpl<E, 7, 4>(v, a, grid, lds, st); break;
+      case 7: return launch_vpl<E, 7, 4>(v, a, grid, lds, st);
       case 8: return launch_vpl<E, 8, 4>(v, a, grid, lds, st);
       case 10: if constexpr (kCap4 >= 10) return launch_vpl<E, 10, 4>(v, a, grid, lds, st); break;
       case 12: if constexpr (kCap4 >= 12) return launch_vpl<E, 12, 4>(v, a, grid, lds, st); break;

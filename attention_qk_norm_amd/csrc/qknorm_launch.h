@@ -108,13 +108,13 @@ struct Variant {
   int rpw = 1;   // rows per one-wavefront team (1, or 2 / 4 for rows of at most 2 slots)
 };
 
-// Slot counts the kernels are compiled for, per workgroup size. FP8 rows
-// in 4-wavefront workgroups get every count up to their cap: an FP8 slot
-// costs about 80 vector instructions per row, so a row of 5 slots (5120
-// columns) run by the 6-slot body would spend a sixth of its arithmetic on
-// an empty slot (2048 x 5120/1024 FP8: 6.77 -> 6.44 us with the exact body).
-constexpr int kVpl4[] = {1, 2, 4, 6, 8, 10, 12, 16};
-constexpr int kVpl4Fp8[] = {1, 2, 3, 4, 5, 6, 7, 8};
+// Slot counts the kernels are compiled for, per workgroup size. In
+// 4-wavefront workgroups every count up to 8 has its own body: a row runs
+// the smallest body that fits, and slots past its own count still cost
+// their loads and arithmetic (an FP8 slot about 80 vector instructions per
+// row). 2048 x 5120/1024 FP8 (5 slots): 6.79 -> 6.48 us with the exact
+// body; 256 x 5120 bf16 in teams of 4 wavefronts (3 slots): 4.25 -> 4.14 us.
+constexpr int kVpl4[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16};
 constexpr int kVpl16[] = {1, 2, 4, 8};
 
 // Most slots per lane for an element type and workgroup size. An FP8 slot
@@ -129,10 +129,7 @@ constexpr int max_slots(int dtype, int nw) {
 // or 0 when none is large enough.
 inline int compiled_vpl(int slots, int nw, int dtype) {
   if (slots > max_slots(dtype, nw)) return 0;
-  if (nw == 4 && dtype == QKNORM_FP8_E4M3) {
-    for (int c : kVpl4Fp8)
-      if (c >= slots) return c;
-  } else if (nw == 4) {
+  if (nw == 4) {
     for (int c : kVpl4)
       if (c >= slots) return c;
   } else if (nw == 16) {

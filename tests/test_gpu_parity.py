@@ -215,6 +215,12 @@ RAGGED = [
     ("f32", 5, 1920, 1920, 40),      # slices of 12 vectors: ragged 4-lane sub-teams
     ("f32", 2048, 200, 200, 5),      # slices of 10 vectors: masked layout, one wavefront per row
     ("f32", 3, 200, 40, 10),         # masked layout over 4 wavefronts (LDS combine)
+    # bodies of odd slot counts: 3 slots in teams of 4 wavefronts; 3 slots
+    # over several rounds; 5 slots with a 1-slot key segment; 7 and 3 slots
+    ("bf16", 128, 5120, 5120, 4),
+    ("bf16", 4096, 1536, 1536, 1),
+    ("bf16", 2048, 2560, 512, 1),
+    ("f32", 1500, 1792, 768, 1),
 ]
 
 
