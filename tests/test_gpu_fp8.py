@@ -90,6 +90,12 @@ SHAPES = [
     (9000, 5120, 3072, 8),
     (12000, 7168, 1024, 1),
     (40, 7168, 7168, 7),
+    # narrow slices in a single round of one-wavefront rows: 8-lane sub-teams
+    # (C4's widths, K = 8); 4- and 1-lane sub-teams; 1-lane sub-teams, 64
+    # slices
+    (2048, 5120, 1024, 8),
+    (2001, 3072, 1536, 48),
+    (2047, 4096, 4096, 64),
 ]
 
 
