@@ -147,6 +147,9 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
   const int vpl = qkn::compiled_vpl(slots, nw, dtype);
   CHECK(vpl > 0, "%s no compiled variant for %d slots", what, slots);
   if (vpl == 0) return;
+  // up to 8 slots in 4-wavefront workgroups, the widest segment runs a body
+  // of exactly its slot count (no empty slots)
+  CHECK(nw != 4 || slots > 8 || vpl == slots, "%s %d slots run by the %d-slot body", what, slots, vpl);
   // several rows per wavefront: every row covered once, no spare workgroups
   for (int mode : {qkn::MODE_STATS, qkn::MODE_FWD}) {
     qkn::Variant v{dtype, mode, vpl, nw, narrow, true, false};
