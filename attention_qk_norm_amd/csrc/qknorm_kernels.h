@@ -379,10 +379,11 @@ __device__ __forceinline__ void load_gamma(typename E::G (&g)[VPL], const Hot& s
 
 // Sums over aligned groups of 2^hl lanes (hl <= 6), every lane of a group
 // receiving the same value: the heads of the headwise form (review,
-// "Layerwise vs. headwise QK-Norm"), and the slices of narrow sub-teams. Within a row of 16 lanes each butterfly step
-// adds the partner group's sum, and the addition is commutative, so the
-// lanes agree bit for bit; groups of 32 and 64 lanes add the row sums read
-// from lanes 0, 16, 32 and 48 in a fixed order.
+// "Layerwise vs. headwise QK-Norm"), and the slices of narrow sub-teams.
+// Within a row of 16 lanes each butterfly step adds the partner group's sum,
+// and the addition is commutative, so the lanes agree bit for bit; groups of
+// 32 and 64 lanes add the row sums read from lanes 0, 16, 32 and 48 in a
+// fixed order.
 template <int V>
 __device__ __forceinline__ void head_sums(float (&q)[V], int hl, int lane) {
   if (hl >= 1) {
@@ -827,9 +828,10 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
 }
 
 // The variant is compiled for VPL slots, the widest segment of the launch;
-// a narrower segment (the key rows of a grouped-query layout) runs the body
-// for VPL/2, VPL/4, ... slots instead, chosen by one uniform branch, so it
-// issues no instructions for slots it does not have.
+// a narrower segment (the key rows of a grouped-query layout) runs the
+// smallest of the bodies for VPL, VPL/2, VPL/4, ... slots (rounded down)
+// that holds its slots, chosen by uniform branches, so key rows of half the
+// query width or less skip the query rows' extra slots.
 template <class E, int V, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW>
 __device__ __forceinline__ void dispatch(const Hot& s, const Tables<VPL>& tb, int wave, int lane,
                                          float* part, u32x4* lds_g) {
