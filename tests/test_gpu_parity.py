@@ -323,6 +323,54 @@ def test_special_rows():
             assert (y1[0] == 0).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_zero_rows_with_zero_eps(dtype):
+    """With eps = 0 a zero row's statistic stays zero and Eq. 1 divides 0 by
+    0: the oracle's fp64 arithmetic gives NaN for every element of that row
+    (and +inf for its inverse RMS), and so does the GPU, fused, headwise and
+    split; the other rows are normalised as usual."""
+    T, H, D, zero = 6, 1024, 128, 2
+    tdt = workloads.DTYPES[dtype]
+    x = workloads.random_rows(T, H, dtype, 95).float()
+    x[zero] = 0.0
+    x = x.to(tdt)
+    g = workloads.random_weights(H, "bf16" if dtype == "fp8" else dtype, 96)
+    live = [t for t in range(T) if t != zero]
+
+    def check(y, ref, what):
+        yh = host64(y)
+        assert np.isnan(ref[zero]).all() and np.isfinite(ref[live]).all(), what
+        assert np.isnan(yh[zero]).all(), (what, yh[zero][:4])
+        assert_parity(y.float()[live], ref[live], tdt, what)  # float: exact for every output type
+
+    for K in (1, 4):
+        say("zero row, eps=0", dtype, "K=%d" % K)
+        y, _ = run_forward(x, None, g, None, 0.0, K)
+        check(y, oracle.forward(x, g, 0.0, K)[0], "forward K=%d" % K)
+        r, _ = qk.inv_rms(gpu(x), None, eps=0.0, num_slices=K)
+        torch.cuda.synchronize()
+        rr = oracle.inv_rms(x, 0.0, K)
+        assert np.isposinf(rr[zero]) and torch.isposinf(r[zero]).item()
+        assert_parity(r[live], rr[live], torch.float32, "inv_rms K=%d" % K)
+        # split path: every slice's partials, then every slice scaled
+        stats = torch.zeros((K, T), dtype=torch.float32, device=DEV)
+        w = H // K
+        xs = gpu(x)
+        for s in range(K):
+            qk.partial_stats(xs[:, s * w:(s + 1) * w], s, K, stats=stats)
+        ys = torch.empty_like(xs)
+        gd = gpu(g)
+        for s in range(K):
+            qk.apply_stats(xs[:, s * w:(s + 1) * w], gd[s * w:(s + 1) * w], stats, H, eps=0.0,
+                           out=ys[:, s * w:(s + 1) * w])
+        torch.cuda.synchronize()
+        check(ys, oracle.forward(x, g, 0.0, K)[0], "split K=%d" % K)
+    say("zero row, eps=0, headwise", dtype)
+    gh = workloads.random_weights(D, "bf16" if dtype == "fp8" else dtype, 97)
+    yh, _ = run_headwise(x, None, gh, None, D, 0.0)
+    check(yh, oracle.qk_headwise(x, x, gh, gh, D, 0.0)[0], "headwise")
+
+
 def test_empty_and_single_tensor():
     z = torch.empty((0, 4096), dtype=torch.bfloat16, device=DEV)
     g = torch.ones(4096, dtype=torch.bfloat16, device=DEV)
