@@ -92,3 +92,51 @@ def test_concurrent_streams():
         torch.cuda.synchronize()
         for o, a in zip(outs, alone):
             assert torch.equal(bits(o), a)
+
+
+def test_shared_context_from_threads():
+    """One context shared by four host threads, each enqueueing on its own
+    stream (validation and planning keep no mutable state): every thread's
+    results equal the single-threaded ones, bit for bit."""
+    import threading
+
+    ctx = qk.Context(0)
+    shapes = [(300, 4096, 1024, "bf16", 8), (2048, 5120, 1024, "fp8", 1), (64, 4096, 4096, "bf16", 1),
+              (129, 1536, 512, "f32", 4)]
+    cases = []
+    for i, (T, hq, hk, dt, K) in enumerate(shapes):
+        gdt = "bf16" if dt == "fp8" else dt
+        q = workloads.random_rows(T, hq, dt, 50 + i).to(DEV)
+        k = workloads.random_rows(T, hk, dt, 60 + i).to(DEV)
+        gq = workloads.random_weights(hq, gdt, 70 + i).to(DEV)
+        gk = workloads.random_weights(hk, gdt, 80 + i).to(DEV)
+        say("single thread", T, hq, hk, dt, K)
+        yq, yk = qk.forward(q, k, gq, gk, eps=1e-6, num_slices=K, ctx=ctx)
+        torch.cuda.synchronize()
+        cases.append(dict(q=q, k=k, gq=gq, gk=gk, K=K, want=(bits(yq), bits(yk)),
+                          out=(torch.empty_like(q), torch.empty_like(k)), stream=torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    failures = []
+
+    def work(c):
+        try:
+            oq, ok = c["out"]
+            for _ in range(20):
+                qk.forward(c["q"], c["k"], c["gq"], c["gk"], eps=1e-6, num_slices=c["K"], out_q=oq, out_k=ok,
+                           ctx=ctx, stream=c["stream"])
+            c["stream"].synchronize()
+        except Exception as e:  # reported by the main thread
+            failures.append(repr(e))
+
+    say("four threads, one context")
+    threads = [threading.Thread(target=work, args=(c,)) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads)
+    torch.cuda.synchronize()
+    assert not failures, failures
+    for c in cases:
+        assert torch.equal(bits(c["out"][0]), c["want"][0])
+        assert torch.equal(bits(c["out"][1]), c["want"][1])
