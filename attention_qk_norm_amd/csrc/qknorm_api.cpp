@@ -175,9 +175,13 @@ bool narrow_plan(const Plan& p) { return p.masked || p.sub_lanes_log2 < 6; }
 // The sub-team size with the fewest slots for a team of 2^wl wavefronts.
 // Sub-teams of whole wavefronts come first (ties go to the smaller one:
 // fewer partials to combine through LDS). Narrower ones are taken only when
-// they need fewer slots (many narrow slices); among those, ties go to the
-// narrower, which holds fewer slices per lane one after another (fewer
-// rounds of group sums).
+// they need fewer slots (many narrow slices). Among those, ties go to the
+// narrowest sub-team of at least 8 lanes, else to the widest: a load
+// instruction reads one run of (sub-team lanes x 16) contiguous bytes per
+// sub-team, and runs shorter than a 128-byte line cost far more than the
+// extra rounds of group sums (16384 x 4096 bf16, 64 slices: 260 us with
+// 2-lane sub-teams against 97 us with 8-lane ones, same 4 slots; 2048 x
+// 5120/1024 bf16, 16 slices: 12.8 us with 4-lane ones against 9.7 us).
 Plan seg_plan(int64_t slice_vec, int K, int wl) {
   Plan best{wl, 6, seg_slots(slice_vec, K, wl, 6), false};
   for (int sl = 7; sl <= 6 + wl; ++sl) {
@@ -187,7 +191,8 @@ Plan seg_plan(int64_t slice_vec, int K, int wl) {
   Plan narrow{wl, 5, seg_slots(slice_vec, K, wl, 5), false};
   for (int sl = 4; sl >= 0; --sl) {
     const int n = seg_slots(slice_vec, K, wl, sl);
-    if (n <= narrow.slots) narrow = Plan{wl, sl, n, false};
+    const bool full_lines = sl >= 3;
+    if (n < narrow.slots || (n == narrow.slots && full_lines)) narrow = Plan{wl, sl, n, false};
   }
   return narrow.slots < best.slots ? narrow : best;
 }

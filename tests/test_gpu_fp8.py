@@ -96,6 +96,7 @@ SHAPES = [
     (2048, 5120, 1024, 8),
     (2001, 3072, 1536, 48),
     (2047, 4096, 4096, 64),
+    (5000, 4096, 4096, 64),    # several rounds, 4-lane sub-teams taking 4 slices in turn
 ]
 
 

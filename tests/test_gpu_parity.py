@@ -221,6 +221,10 @@ RAGGED = [
     ("bf16", 4096, 1536, 1536, 1),
     ("bf16", 2048, 2560, 512, 1),
     ("f32", 1500, 1792, 768, 1),
+    # many narrow slices over several rounds of wavefronts: 8-lane sub-teams
+    # taking 4 (64 slices) or 2 (16 slices) slices in turn
+    ("bf16", 5000, 4096, 4096, 64),
+    ("bf16", 2048, 5120, 1024, 16),
 ]
 
 
