@@ -155,6 +155,7 @@ struct Plan {
   int sub_lanes_log2 = 6;  // sub-team: 2^sub_lanes_log2 lanes deal one slice at a time
   int slots = 0;
   bool masked = false;
+  int min_slots = 0;       // seg_plan: the fewest slots any sub-team layout of this team needs
 };
 
 // Slots per lane of the segmented layout: teams of 2^wl wavefronts, split
@@ -172,29 +173,42 @@ Plan masked_plan(int64_t nvec, int wl) { return Plan{wl, 6 + wl, plain_slots(nve
 // Plans served by the kernels for slices narrower than a wavefront.
 bool narrow_plan(const Plan& p) { return p.masked || p.sub_lanes_log2 < 6; }
 
-// The sub-team size with the fewest slots for a team of 2^wl wavefronts.
-// Sub-teams of whole wavefronts come first (ties go to the smaller one:
-// fewer partials to combine through LDS). Narrower ones are taken only when
-// they need fewer slots (many narrow slices). Among those, ties go to the
-// narrowest sub-team of at least 8 lanes, else to the widest: a load
-// instruction reads one run of (sub-team lanes x 16) contiguous bytes per
-// sub-team, and runs shorter than a 128-byte line cost far more than the
-// extra rounds of group sums (16384 x 4096 bf16, 64 slices: 260 us with
-// 2-lane sub-teams against 97 us with 8-lane ones, same 4 slots; 2048 x
-// 5120/1024 bf16, 16 slices: 12.8 us with 4-lane ones against 9.7 us).
-Plan seg_plan(int64_t slice_vec, int K, int wl) {
+// Relative cost of a layout: its slots, weighted by the length of the
+// contiguous run a load instruction reads per sub-team ((sub-team lanes x
+// 16) bytes, or a whole wavefront's for sub-teams of whole wavefronts).
+// Runs shorter than a 128-byte line cost more than the slots saved; the
+// weights (in quarters: 1, 1.25, 2.5, 4 for runs of >= 128, 64, 32 and 16
+// bytes) follow what equal-slot layouts measured on MI355X: 16384 x
+// 4096/4096 bf16, 64 slices: 260 us with 2-lane sub-teams against 97 us with
+// 8-lane ones; 32 slices: 109 against 87 us with 4-lane against 8-lane ones.
+int layout_cost(int slots, int sl) { return slots * (sl >= 3 ? 4 : sl == 2 ? 5 : sl == 1 ? 10 : 16); }
+
+// The sub-team size for a team of 2^wl wavefronts. Sub-teams of whole
+// wavefronts come first (fewest slots; ties go to the smaller sub-team: fewer
+// partials to combine through LDS). Narrower ones serve many narrow slices:
+// among those within `cap` slots the least layout_cost wins (ties to the
+// narrowest of at least 8 lanes, which takes fewer rounds of group sums), and
+// it replaces the whole-wavefront layout only when it costs less.
+Plan seg_plan(int64_t slice_vec, int K, int wl, int cap) {
   Plan best{wl, 6, seg_slots(slice_vec, K, wl, 6), false};
   for (int sl = 7; sl <= 6 + wl; ++sl) {
     const int n = seg_slots(slice_vec, K, wl, sl);
     if (n < best.slots) best = Plan{wl, sl, n, false};
   }
-  Plan narrow{wl, 5, seg_slots(slice_vec, K, wl, 5), false};
-  for (int sl = 4; sl >= 0; --sl) {
+  int fewest = best.slots;
+  Plan narrow{};
+  for (int sl = 5; sl >= 0; --sl) {
     const int n = seg_slots(slice_vec, K, wl, sl);
-    const bool full_lines = sl >= 3;
-    if (n < narrow.slots || (n == narrow.slots && full_lines)) narrow = Plan{wl, sl, n, false};
+    fewest = n < fewest ? n : fewest;
+    if (n > cap) continue;
+    const int c = layout_cost(n, sl);
+    const int cn = narrow.slots ? layout_cost(narrow.slots, narrow.sub_lanes_log2) : -1;
+    if (cn < 0 || c < cn || (c == cn && sl >= 3)) narrow = Plan{wl, sl, n, false};
   }
-  return narrow.slots < best.slots ? narrow : best;
+  Plan pick = (narrow.slots && layout_cost(narrow.slots, narrow.sub_lanes_log2) < layout_cost(best.slots, 6))
+                  ? narrow : best;
+  pick.min_slots = fewest;
+  return pick;
 }
 
 // Choose the team size for one segment by its row width. The smallest team
@@ -208,11 +222,11 @@ bool plan_segment(int64_t nvec, int K, int max_wl, int cap, int forced_wl, Plan*
   const int lo = forced_wl >= 0 ? forced_wl : 0;
   const int hi = forced_wl >= 0 ? forced_wl : max_wl;
   for (int wl = lo; wl <= hi; ++wl) {
-    const Plan p = seg_plan(slice_vec, K, wl);
+    const Plan p = seg_plan(slice_vec, K, wl, cap);
     // slices much narrower than a sub-team leave most of each slot's lanes
     // empty: the masked layout then issues half the loads or fewer
     const int m = plain_slots(nvec, wl);
-    if (m <= cap && 2 * m <= p.slots) {
+    if (m <= cap && 2 * m <= p.min_slots) {
       *out = masked_plan(nvec, wl);
       return true;
     }
@@ -287,7 +301,7 @@ int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int
       for (int i = 0; i < nseg; ++i) {
         if (plans[i].wpr_log2 != 0 || plans[i].slots < 8) continue;
         const Plan p = plans[i].masked ? masked_plan(in[i].nvec, 1)
-                                       : seg_plan(in[i].nvec / in[i].K, in[i].K, 1);
+                                       : seg_plan(in[i].nvec / in[i].K, in[i].K, 1, cap4);
         if (p.slots <= cap4) plans[i] = p;
       }
       return QKNORM_OK;
@@ -302,7 +316,7 @@ int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int
         const int wl = plans[i].wpr_log2 + 1;
         if (wl > 2) continue;
         plans[i] = plans[i].masked ? masked_plan(in[i].nvec, wl)
-                                   : seg_plan(in[i].nvec / in[i].K, in[i].K, wl);
+                                   : seg_plan(in[i].nvec / in[i].K, in[i].K, wl, cap4);
         widened = true;
       }
       if (!widened) break;
