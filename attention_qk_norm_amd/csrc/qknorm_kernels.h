@@ -263,6 +263,24 @@ __device__ __forceinline__ float lane_value(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
+// S plus the values of lanes l0, l0 + step, ..., n of them, added one after
+// another in that order (every lane gets the same result). The lane reads go
+// out four at a time ahead of their additions.
+__device__ __forceinline__ float add_lanes_in_order(float S, float v, int l0, int step, int n) {
+  int i = 0;
+  for (; i + 4 <= n; i += 4) {
+    const int l = l0 + i * step;
+    const float a = lane_value(v, l), b = lane_value(v, l + step), c = lane_value(v, l + 2 * step),
+                e = lane_value(v, l + 3 * step);
+    S += a;
+    S += b;
+    S += c;
+    S += e;
+  }
+  for (; i < n; ++i) S += lane_value(v, l0 + i * step);
+  return S;
+}
+
 // Sum over the 64 lanes of a wavefront; every lane receives the same value.
 // Must be called with all 64 lanes active.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -471,12 +489,11 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
         const int last = min(k0 + (1 << nsw_log2), s.lay_k);
         if (L.wpr == 1) {
           // round-major, sub-team-minor: ascending k
-          for (int k = k0, l = 0; k < last; ++k, l += 1 << sl) S += lane_value(g[0], l);
+          S = add_lanes_in_order(S, g[0], 0, 1 << sl, last - k0);
         } else {
-          for (int k = k0, l = 0; k < last; ++k, l += 1 << sl) {
-            const float P = lane_value(g[0], l);
-            if (lane == 0) part[w0 * kWave + k] = P;
-          }
+          // the first lane of each sub-team publishes its slice's partial
+          const int k = k0 + (lane >> sl);
+          if ((lane & ((1 << sl) - 1)) == 0 && k < last) part[w0 * kWave + k] = g[0];
         }
         p = 0.f;
         ++round;
@@ -534,7 +551,7 @@ __device__ __forceinline__ float row_stat(const u32x4 (&d)[VPL], const Hot& s, c
         Pk = part[w0 * kWave + lane];
       }
     }
-    for (int k = 0; k < s.lay_k; ++k) S += lane_value(Pk, k);
+    S = add_lanes_in_order(S, Pk, 0, 1, s.lay_k);
     if (reuse) __syncthreads();  // `part` is free again
   }
   return S;
@@ -619,7 +636,7 @@ __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename
     // lane k fetches partial k; then they are added in ascending k
     float pk = 0.f;
     if (live && lane < s.comb_k) pk = s.stats_in[static_cast<int64_t>(lane) * s.T + row];
-    for (int k = 0; k < s.comb_k; ++k) S += lane_value(pk, k);
+    S = add_lanes_in_order(S, pk, 0, 1, s.comb_k);
   } else {
     S = row_stat<E, VPL, NARROW>(d, s, L, wave, lane, part, reuse);
   }
