@@ -270,12 +270,16 @@ struct SegIn {
 //  - fewer than 2 rows per SIMD (decode-sized batches): teams widen, up to
 //    one workgroup per row, until there are 2 wavefronts per SIMD, so each
 //    row's loads are spread over more wavefronts and finish sooner;
-//  - 8 or more rows per SIMD (long prefill launches, several rounds of
-//    wavefronts per SIMD): a row that would take a wavefront 8 or more slots
-//    is shared by two wavefronts, so each holds half a row and its writes
-//    start sooner after its reads (bf16 16384 x 4096, 8 slots: 3% faster);
-//    with fewer slots one wavefront per row stays faster (FP8 16384 x 4096,
-//    4 slots: 47.7 us against 50.7 us with two);
+//  - 8 or more wavefronts per SIMD, counting each segment's team (long
+//    prefill launches, several rounds of wavefronts per SIMD): a row that
+//    would take one wavefront 8 or more slots is shared by two wavefronts,
+//    so each holds half a row and its writes start sooner after its reads
+//    (bf16 16384 x 4096, 8 slots: 3% faster); with fewer slots one
+//    wavefront per row stays faster (FP8 16384 x 4096, 4 slots: 47.7 us
+//    against 50.7 us with two). Counting wavefronts rather than rows
+//    matters when the query rows already take teams: 3632 x 32768/4096
+//    bf16, whose key rows then take two wavefronts instead of one with 8
+//    slots, 100.0 -> 95.3 us;
 //  - in between, every row's loads are issued in the first round, and one
 //    wavefront per row is fastest.
 int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int64_t T, Plan* plans, int* nw) {
@@ -297,7 +301,9 @@ int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int
   if (!ok) return QKNORM_ERR_SHAPE;
   if (fl < 0) {
     const int64_t simds = int64_t{4} * ctx->num_cus;
-    if (T * nseg >= 8 * simds) {
+    int64_t team_waves = 0;
+    for (int i = 0; i < nseg; ++i) team_waves += T << plans[i].wpr_log2;
+    if (team_waves >= 8 * simds) {
       for (int i = 0; i < nseg; ++i) {
         if (plans[i].wpr_log2 != 0 || plans[i].slots < 8) continue;
         const Plan p = plans[i].masked ? masked_plan(in[i].nvec, 1)

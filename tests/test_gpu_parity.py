@@ -225,6 +225,9 @@ RAGGED = [
     # taking 4 (64 slices) or 2 (16 slices) slices in turn
     ("bf16", 5000, 4096, 4096, 64),
     ("bf16", 2048, 5120, 1024, 16),
+    # query rows in teams of 4 wavefronts make several rounds of wavefronts,
+    # so the 8-slot key rows take two wavefronts each
+    ("bf16", 2048, 32768, 4096, 1),
 ]
 
 
