@@ -295,7 +295,29 @@ int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int
     ok = true;
     for (int i = 0; i < nseg && ok; ++i) ok = plan_segment(in[i].nvec, in[i].K, 4, cap16, fl, &plans[i]);
     *nw = 16;
-    return ok ? QKNORM_OK : QKNORM_ERR_SHAPE;
+    if (!ok) return QKNORM_ERR_SHAPE;
+    // Rows this wide take teams of up to 16 wavefronts, so the launch makes
+    // several rounds of wavefronts even for modest T; a segment whose rows
+    // would take 8 or more slots per lane (the key rows beside such query
+    // rows) then widens its team while it keeps 2 or more slots. 1808 x
+    // 65536/8192 bf16: 121.8 -> 103.9 us (8192-column key rows in teams of
+    // 16 wavefronts instead of 2).
+    if (fl < 0) {
+      const int64_t simds = int64_t{4} * ctx->num_cus;
+      int64_t team_waves = 0;
+      for (int i = 0; i < nseg; ++i) team_waves += T << plans[i].wpr_log2;
+      if (team_waves >= 8 * simds) {
+        for (int i = 0; i < nseg; ++i) {
+          if (plans[i].masked || plans[i].slots < 8) continue;
+          while (plans[i].wpr_log2 < 4 && plans[i].slots >= 2) {
+            const Plan p = seg_plan(in[i].nvec / in[i].K, in[i].K, plans[i].wpr_log2 + 1, cap16);
+            if (p.slots > cap16 || p.masked) break;
+            plans[i] = p;
+          }
+        }
+      }
+    }
+    return QKNORM_OK;
   }
   *nw = 4;
   if (!ok) return QKNORM_ERR_SHAPE;

@@ -228,6 +228,10 @@ RAGGED = [
     # query rows in teams of 4 wavefronts make several rounds of wavefronts,
     # so the 8-slot key rows take two wavefronts each
     ("bf16", 2048, 32768, 4096, 1),
+    # 16-wavefront workgroups: 65536-column query rows, and 8192-column key
+    # rows widened to teams of 16 wavefronts (one slot each); fp32 likewise
+    ("bf16", 600, 65536, 8192, 1),
+    ("f32", 1200, 32768, 4096, 2),
 ]
 
 
