@@ -272,11 +272,11 @@ struct SegIn {
 //    row's loads are spread over more wavefronts and finish sooner;
 //  - 8 or more wavefronts per SIMD, counting each segment's team (long
 //    prefill launches, several rounds of wavefronts per SIMD): a row that
-//    would take one wavefront 8 or more slots is shared by two wavefronts,
-//    so each holds half a row and its writes start sooner after its reads
-//    (bf16 16384 x 4096, 8 slots: 3% faster); with fewer slots one
-//    wavefront per row stays faster (FP8 16384 x 4096, 4 slots: 47.7 us
-//    against 50.7 us with two). Counting wavefronts rather than rows
+//    would take one wavefront 16 or more slots, or 8 or more when every
+//    segment's rows would, is shared by two wavefronts, so each holds half
+//    a row and its writes start sooner after its reads (bf16 16384 x 4096,
+//    8 slots: 3% faster); with fewer slots one wavefront per row stays
+//    faster (FP8 16384 x 4096, 4 slots: 47.7 us against 50.7 us with two). Counting wavefronts rather than rows
 //    matters when the query rows already take teams: 3632 x 32768/4096
 //    bf16, whose key rows then take two wavefronts instead of one with 8
 //    slots, 100.0 -> 95.3 us;
@@ -326,8 +326,15 @@ int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int
     int64_t team_waves = 0;
     for (int i = 0; i < nseg; ++i) team_waves += T << plans[i].wpr_log2;
     if (team_waves >= 8 * simds) {
+      // rows of 8-15 slots widen only when every segment's rows do (both
+      // 8-slot segments of 16384 x 4096/4096 bf16: 86.7 -> 84.3 us); beside
+      // key rows that stay with one wavefront they stay too (26208 x
+      // 4096/1024 bf16: 88.9 us widened, 85.3 us not); 16 slots always widen
+      bool all = true;
+      for (int i = 0; i < nseg; ++i) all = all && (plans[i].wpr_log2 != 0 || plans[i].slots >= 8);
       for (int i = 0; i < nseg; ++i) {
         if (plans[i].wpr_log2 != 0 || plans[i].slots < 8) continue;
+        if (plans[i].slots < 16 && !all) continue;
         const Plan p = plans[i].masked ? masked_plan(in[i].nvec, 1)
                                        : seg_plan(in[i].nvec / in[i].K, in[i].K, 1, cap4);
         if (p.slots <= cap4) plans[i] = p;

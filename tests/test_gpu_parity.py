@@ -228,6 +228,9 @@ RAGGED = [
     # query rows in teams of 4 wavefronts make several rounds of wavefronts,
     # so the 8-slot key rows take two wavefronts each
     ("bf16", 2048, 32768, 4096, 1),
+    # several rounds: 8-slot query rows beside 2-slot key rows keep one
+    # wavefront per row
+    ("bf16", 5000, 4096, 1024, 1),
     # 16-wavefront workgroups: 65536-column query rows, and 8192-column key
     # rows widened to teams of 16 wavefronts (one slot each); fp32 likewise
     ("bf16", 600, 65536, 8192, 1),
