@@ -276,10 +276,10 @@ struct SegIn {
 //    segment's rows would, is shared by two wavefronts, so each holds half
 //    a row and its writes start sooner after its reads (bf16 16384 x 4096,
 //    8 slots: 3% faster); with fewer slots one wavefront per row stays
-//    faster (FP8 16384 x 4096, 4 slots: 47.7 us against 50.7 us with two). Counting wavefronts rather than rows
-//    matters when the query rows already take teams: 3632 x 32768/4096
-//    bf16, whose key rows then take two wavefronts instead of one with 8
-//    slots, 100.0 -> 95.3 us;
+//    faster (FP8 16384 x 4096, 4 slots: 47.7 us against 50.7 us with two).
+//    Counting wavefronts rather than rows matters when the query rows
+//    already take teams: 3632 x 32768/4096 bf16, whose key rows then take
+//    two wavefronts instead of one with 8 slots, 100.0 -> 95.3 us;
 //  - in between, every row's loads are issued in the first round, and one
 //    wavefront per row is fastest.
 int plan_launch(const qknorm_ctx* ctx, int dtype, const SegIn* in, int nseg, int64_t T, Plan* plans, int* nw) {
