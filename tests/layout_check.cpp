@@ -227,6 +227,38 @@ static void run_headwise(int64_t T, int64_t hq, int64_t hk, int64_t D, int force
   }
 }
 
+// The plan of one launch (automatic schedule, 256 compute units) as one
+// line: what the tests pin for the benchmark workloads, so that a change of
+// the planner that moves one of them shows up.
+static void print_plan(const char* name, int dtype, int64_t T, int64_t hq, int64_t hk, int K) {
+  qknorm_ctx ctx{0, 256, qknorm_options{0, 0, 0}};
+  const int64_t ve = vec_elems(dtype);
+  SegIn in[2] = {{hq / ve, K}, {hk / ve, K}};
+  Plan plans[2];
+  int nw = 4;
+  if (plan_launch(&ctx, dtype, in, 2, T, plans, &nw) != QKNORM_OK) {
+    std::printf("plan %s: refused\n", name);
+    return;
+  }
+  qkn::Args a{};
+  a.T = T;
+  bool narrow = false;
+  int slots = 0;
+  for (int i = 0; i < 2; ++i) {
+    narrow = narrow || narrow_plan(plans[i]);
+    fill_layout(&a.seg[i], plans[i], nw, in[i].nvec, K, T);
+    share_gamma(&a.seg[i], dtype);
+    slots = a.seg[i].nslot > slots ? a.seg[i].nslot : slots;
+  }
+  qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw, dtype), nw, narrow, true, false};
+  rows_per_wave(&ctx, &v, &a, 2);
+  std::printf("plan %s: nw=%d body=%d narrow=%d rows_per_wave=%d", name, nw, v.vpl, narrow ? 1 : 0, v.rpw);
+  for (int i = 0; i < 2; ++i)
+    std::printf(" | %s team=%d sub_lanes=%d slots=%d masked=%d", i ? "k" : "q", 1 << plans[i].wpr_log2,
+                1 << plans[i].sub_lanes_log2, plans[i].slots, plans[i].masked ? 1 : 0);
+  std::printf("\n");
+}
+
 int main() {
   int cases = 0;
   const int64_t widths[] = {8, 24, 64, 96, 200, 256, 512, 1000, 1024, 1032, 1280, 1536, 2048,
@@ -262,6 +294,17 @@ int main() {
             cases += 2;
           }
       }
+  print_plan("c1 K=1", QKNORM_F32, 4, 256, 256, 1);
+  print_plan("c1 K=4", QKNORM_F32, 4, 256, 256, 4);
+  print_plan("c2 K=1", QKNORM_BF16, 64, 4096, 4096, 1);
+  print_plan("c3 K=4", QKNORM_BF16, 256, 5120, 5120, 4);
+  print_plan("c3 K=1", QKNORM_BF16, 256, 5120, 5120, 1);
+  print_plan("c4 K=1", QKNORM_BF16, 2048, 5120, 1024, 1);
+  print_plan("c5 K=8", QKNORM_BF16, 16384, 4096, 4096, 8);
+  print_plan("c5 K=1", QKNORM_BF16, 16384, 4096, 4096, 1);
+  print_plan("c4f8 K=1", QKNORM_FP8_E4M3, 2048, 5120, 1024, 1);
+  print_plan("c5f8 K=8", QKNORM_FP8_E4M3, 16384, 4096, 4096, 8);
+  print_plan("c5f8 K=1", QKNORM_FP8_E4M3, 16384, 4096, 4096, 1);
   std::printf("segments: %ld whole-wavefront sub-teams, %ld narrower sub-teams, %ld masked\n", g_layouts[0],
               g_layouts[1], g_layouts[2]);
   std::printf("%d cases, %d failures\n", cases, failures);
