@@ -97,6 +97,11 @@ SHAPES = [
     (2001, 3072, 1536, 48),
     (2047, 4096, 4096, 64),
     (5000, 4096, 4096, 64),    # several rounds, 4-lane sub-teams taking 4 slices in turn
+    # grouped-query rows: 2-wavefront query teams sharing a narrow-slice launch
+    # with 8-lane key sub-teams, over several rounds; 16-wavefront query teams
+    # beside 2-wavefront key teams
+    (3000, 16384, 2048, 8),
+    (600, 65536, 8192, 1),
 ]
 
 

@@ -205,6 +205,8 @@ RAGGED = [
     ("bf16", 4, 16384, 16384, 8),    # wider than one wavefront's 16 slots
     ("bf16", 3, 65536, 8, 1),        # widest accepted row, with a tiny key row
     ("bf16", 2, 32768, 32768, 16),
+    ("bf16", 3000, 16384, 2048, 8),  # 2-wavefront query teams in a narrow-slice launch with 8-lane key sub-teams
+    ("f32", 3000, 4096, 1024, 8),    # 16-slot query rows beside 8-lane key sub-teams
     ("f32", 1, 4, 4, 1),
     ("f32", 6, 260, 12, 1),
     ("f32", 33, 256, 256, 4),
