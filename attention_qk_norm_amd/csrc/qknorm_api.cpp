@@ -568,6 +568,17 @@ int qknorm_forward(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q, 
   int nw = 4;
   st = plan_launch(ctx, dtype, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) return st;
+  // When only one tensor's rows need the narrow-slice kernels, a large pair
+  // runs as two launches, so the other tensor keeps the plain kernels (their
+  // registers cost the narrow ones 5-9% on wide query rows: 16384 tokens of
+  // 16384/2048 bf16 columns in 8 slices, 218 -> 199 us); below 2^23 vectors
+  // the second launch costs more than it saves (about 1.5 us).
+  if (nseg == 2 && narrow_plan(plans[0]) != narrow_plan(plans[1]) &&
+      T * (in[0].nvec + in[1].nvec) >= (int64_t{1} << 23)) {
+    st = qknorm_forward(ctx, dtype, T, q, nullptr, gamma_q, nullptr, eps, num_slices, stream);
+    if (st != QKNORM_OK) return st;
+    return qknorm_forward(ctx, dtype, T, k, nullptr, gamma_k, nullptr, eps, num_slices, stream);
+  }
 
   bool narrow = false;
   for (int i = 0; i < nseg; ++i) narrow = narrow || narrow_plan(plans[i]);

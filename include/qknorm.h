@@ -122,11 +122,12 @@ int qknorm_create_ex(qknorm_ctx **ctx_out, int device, const qknorm_options *opt
 int qknorm_destroy(qknorm_ctx *ctx);
 
 /*
- * Fused layerwise QK-Norm over the query rows and the key rows of T tokens,
- * in one kernel launch (SwiftQK review Eq. 1 per tensor; the K-slice scalar
- * statistic of section 4b, Eqs. 3-6). Each row is read from memory once and
- * written once: the row stays in registers between the statistic and the
- * scaling.
+ * Fused layerwise QK-Norm over the query rows and the key rows of T tokens
+ * (SwiftQK review Eq. 1 per tensor; the K-slice scalar statistic of section
+ * 4b, Eqs. 3-6), normally in one kernel launch; a large pair of which only
+ * one tensor needs the narrow-slice kernels takes one launch per tensor, in
+ * order on the stream. Each row is read from memory once and written once:
+ * the row stays in registers between the statistic and the scaling.
  *
  *   dtype      element type of q, k, gamma_q and gamma_k
  *   T          tokens (rows of q and of k); T == 0 returns QKNORM_OK at once

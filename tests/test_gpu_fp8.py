@@ -101,6 +101,7 @@ SHAPES = [
     # with 8-lane key sub-teams, over several rounds; 16-wavefront query teams
     # beside 2-wavefront key teams
     (3000, 16384, 2048, 8),
+    (7300, 16384, 2048, 8),    # past 2^23 vectors: one launch per tensor
     (600, 65536, 8192, 1),
 ]
 

@@ -206,6 +206,7 @@ RAGGED = [
     ("bf16", 3, 65536, 8, 1),        # widest accepted row, with a tiny key row
     ("bf16", 2, 32768, 32768, 16),
     ("bf16", 3000, 16384, 2048, 8),  # 2-wavefront query teams in a narrow-slice launch with 8-lane key sub-teams
+    ("bf16", 3700, 16384, 2048, 8),  # the same pair past 2^23 vectors: one launch per tensor
     ("f32", 3000, 4096, 1024, 8),    # 16-slot query rows beside 8-lane key sub-teams
     ("f32", 1, 4, 4, 1),
     ("f32", 6, 260, 12, 1),
