@@ -22,7 +22,8 @@ def bits(t):
 
 
 def test_graph_capture_and_replay():
-    """Fused forward (K = 4), headwise and inverse RMS captured in one graph;
+    """Fused forward (K = 4), headwise and inverse RMS captured in one graph,
+    with a grouped-query pair large enough to take one launch per tensor;
     each replay, with unrelated eager work and a synchronisation in between,
     matches the eager call on fresh inputs copied into the captured buffers."""
     T, Hq, Hk = 96, 4096, 1024
@@ -35,15 +36,27 @@ def test_graph_capture_and_replay():
     hq, hk = torch.empty_like(q), torch.empty_like(k)
     rq = torch.empty(T, device=DEV)
     rk = torch.empty(T, device=DEV)
+    # 3700 x 16384/2048 in 8 slices: only the key rows need the narrow-slice
+    # kernels, and the pair holds over 2^23 vectors
+    TB, BQ, BK = 3700, 16384, 2048
+    bq0 = workloads.random_rows(TB, BQ, "bf16", 20).to(DEV)
+    bk0 = workloads.random_rows(TB, BK, "bf16", 21).to(DEV)
+    bq, bk = torch.empty_like(bq0), torch.empty_like(bk0)
+    gbq = workloads.random_weights(BQ, "bf16", 22).to(DEV)
+    gbk = workloads.random_weights(BK, "bf16", 23).to(DEV)
+    ybq, ybk = torch.empty_like(bq0), torch.empty_like(bk0)
 
     def calls(stream):
         qk.forward(q, k, gq, gk, eps=1e-6, num_slices=4, out_q=yq, out_k=yk, stream=stream)
         qk.forward_headwise(q, k, hg, hg, 128, eps=1e-6, out_q=hq, out_k=hk, stream=stream)
         qk.inv_rms(q, k, eps=1e-6, num_slices=4, out_q=rq, out_k=rk, stream=stream)
+        qk.forward(bq, bk, gbq, gbk, eps=1e-6, num_slices=8, out_q=ybq, out_k=ybk, stream=stream)
 
     s = torch.cuda.Stream()
     q.copy_(workloads.random_rows(T, Hq, "bf16", 10).to(DEV))
     k.copy_(workloads.random_rows(T, Hk, "bf16", 11).to(DEV))
+    bq.copy_(bq0)
+    bk.copy_(bk0)
     torch.cuda.synchronize()
     with torch.cuda.stream(s):  # warm the stream, as capture requires
         calls(s)
@@ -56,15 +69,17 @@ def test_graph_capture_and_replay():
     for rep in range(4):
         q.copy_(workloads.random_rows(T, Hq, "bf16", 100 + rep).to(DEV))
         k.copy_(workloads.random_rows(T, Hk, "bf16", 200 + rep).to(DEV))
+        bq.copy_(bq0.roll(rep + 1, dims=0))
+        bk.copy_(bk0.roll(rep + 1, dims=0))
         torch.cuda.synchronize()
         say("replay", rep)
         g.replay()
         torch.cuda.synchronize()
-        got = [bits(t) for t in (yq, yk, hq, hk, rq, rk)]
+        got = [bits(t) for t in (yq, yk, hq, hk, rq, rk, ybq, ybk)]
         junk = torch.randn(1 << 20, device=DEV).sum()  # unrelated eager work between replays
         calls(torch.cuda.current_stream())
         torch.cuda.synchronize()
-        want = [bits(t) for t in (yq, yk, hq, hk, rq, rk)]
+        want = [bits(t) for t in (yq, yk, hq, hk, rq, rk, ybq, ybk)]
         for a, b in zip(got, want):
             assert torch.equal(a, b), rep
         del junk
