@@ -170,14 +170,31 @@ def gamma_dtype(row_dtype):
 
 
 def _rows_of(x, y):
-    """Describe 2-D row tensors x (input) and y (output) as a Rows struct."""
+    """Describe 2-D row tensors x (input) and y (output) as a Rows struct.
+    The C ABI sees only pointers, so the output's shape and dtype are checked
+    here: a smaller or differently typed y would be written past its end."""
     if x.dim() != 2 or (y is not None and y.dim() != 2):
         raise ValueError("rows must be 2-D [T, width] tensors")
+    if y is not None and (tuple(y.shape) != tuple(x.shape) or y.dtype != x.dtype):
+        raise ValueError("the output must have the input's shape %s and dtype %s, got %s %s"
+                         % (tuple(x.shape), x.dtype, tuple(y.shape), y.dtype))
     if x.stride(1) != 1 or (y is not None and y.stride(1) != 1):
         raise ValueError("each row must be contiguous (stride 1 along the width)")
     yy = y if y is not None else x
     return Rows(x.data_ptr(), yy.data_ptr(), x.shape[1], x.stride(0) if x.shape[0] > 1 else x.shape[1],
                 yy.stride(0) if yy.shape[0] > 1 else yy.shape[1])
+
+
+def _on_one_gpu(*tensors):
+    """Every tensor a call hands to the library must be GPU memory of one
+    device: the kernels dereference the pointers on that device."""
+    ts = [t for t in tensors if t is not None]
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU (device type 'cuda'), got %s" % dev)
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError("all tensors of a call must be on %s, got one on %s" % (dev, t.device))
 
 
 def _stream_of(t, stream):
@@ -216,6 +233,7 @@ def _qk_rows(q, k, gamma_q, gamma_k, gamma_width, out_q, out_k):
                 not g.is_contiguous():
             raise ValueError("gamma must be a contiguous 1-D %s tensor with %d weights"
                              % (gamma_dtype(x.dtype), gamma_width(x)))
+    _on_one_gpu(q, out_q, gamma_q, k, out_k, gamma_k if k is not None else None)
     return dt, T, rq, rk, out_q, out_k
 
 
@@ -275,6 +293,7 @@ def inv_rms(q, k=None, eps=1e-6, num_slices=1, out_q=None, out_k=None, ctx=None,
         if o.dtype != torch.float32 or o.shape != (T,) or not o.is_contiguous():
             raise ValueError("inverse-RMS outputs are contiguous float32 [T] tensors")
         outs.append(o)
+    _on_one_gpu(q, k, outs[0], outs[1])
     c = _ctx_of(q, ctx)
     st = lib().qknorm_inv_rms(c.handle, dt, T, ctypes.byref(rq), ctypes.byref(rk) if rk is not None else None,
                               float(eps), int(num_slices), outs[0].data_ptr(),
@@ -295,6 +314,7 @@ def partial_stats(x_slice, slice_index, num_slices, stats=None, ctx=None, stream
         stats = torch.zeros((num_slices, T), dtype=torch.float32, device=x_slice.device)
     if stats.dtype != torch.float32 or stats.shape != (num_slices, T) or not stats.is_contiguous():
         raise ValueError("stats must be a contiguous float32 [num_slices, T] tensor")
+    _on_one_gpu(x_slice, stats)
     c = _ctx_of(x_slice, ctx)
     st = lib().qknorm_partial_stats(c.handle, dt, T, x_slice.data_ptr(),
                                     x_slice.stride(0) if T > 1 else x_slice.shape[1],
@@ -316,8 +336,10 @@ def apply_stats(x_slice, gamma_slice, stats, h_total, eps=1e-6, out=None, ctx=No
     if stats.dtype != torch.float32 or stats.dim() != 2 or stats.shape[1] != T or not stats.is_contiguous():
         raise ValueError("stats must be a contiguous float32 [K, T] tensor")
     if gamma_slice.dtype != gamma_dtype(x_slice.dtype) or gamma_slice.dim() != 1 or \
-            not gamma_slice.is_contiguous():
-        raise ValueError("gamma_slice must be a contiguous 1-D %s tensor" % gamma_dtype(x_slice.dtype))
+            gamma_slice.shape[0] != x_slice.shape[1] or not gamma_slice.is_contiguous():
+        raise ValueError("gamma_slice must be a contiguous 1-D %s tensor with %d weights"
+                         % (gamma_dtype(x_slice.dtype), x_slice.shape[1]))
+    _on_one_gpu(x_slice, out, gamma_slice, stats)
     c = _ctx_of(x_slice, ctx)
     st = lib().qknorm_apply_stats(c.handle, dt, T, ctypes.byref(r), gamma_slice.data_ptr(),
                                   stats.data_ptr(), stats.shape[0], int(h_total), float(eps),

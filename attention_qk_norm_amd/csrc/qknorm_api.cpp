@@ -381,6 +381,9 @@ void fill_layout(qkn::Seg* s, const Plan& p, int nw, int64_t nvec, int K, int64_
   s->inv_slice_vec = 1.0f / static_cast<float>(slice_vec);
   s->lds_gamma = 0;
   s->flush_mask = 0;
+  // no slot needs a lane test (qkn::slot_offset)
+  s->dense = (p.masked || K == 1 || slice_vec % ns == 0) ? 1 : 0;
+  s->tail_lanes = static_cast<int32_t>(ns);
   for (int j = 0; j < qkn::kMaxSlots; ++j) {
     s->slot_base[j] = 0;
     s->slot_lim[j] = 0;
@@ -395,6 +398,7 @@ void fill_layout(qkn::Seg* s, const Plan& p, int nw, int64_t nvec, int K, int64_
   }
   const int64_t sps = ceil_div(slice_vec, ns);  // slots per slice
   s->nslot = static_cast<int32_t>(ceil_div(K, nsub) * sps);
+  s->tail_lanes = static_cast<int32_t>(slice_vec - (sps - 1) * ns);
   for (int j = 0; j < s->nslot; ++j) {
     const int64_t i = j / sps, ij = j % sps;  // the sub-team's i-th slice, its ij-th slot
     const int64_t left = slice_vec - ij * ns;

@@ -49,7 +49,7 @@ constexpr int kWave = 64;
 // zeros and their stores are dropped by the hardware range check, so ragged
 // slots, partial teams and rows past T need no branches.
 constexpr int kRsrcConfig = 0x00020000;  // raw, untyped, 32-bit data format
-constexpr uint32_t kOutside = 0x80000000u;
+constexpr uint32_t kOutside = kOutsideOffset;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
@@ -311,7 +311,7 @@ struct Hot {
   float* stats_out;
   int64_t x_stride, y_stride, T;
   int rows_per_wg, nwg, nslot, wpr_log2, sub_lanes_log2, lds_gamma, lay_k, comb_k, masked, slice_vec,
-      head_log2, emit_rinv;
+      head_log2, emit_rinv, dense, tail_lanes;
   uint32_t row_bytes, flush_mask;
   float inv_slice_vec, h, inv_h, eps;
 
@@ -320,28 +320,25 @@ struct Hot {
         x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
         nslot(s.nslot), wpr_log2(s.wpr_log2), sub_lanes_log2(s.sub_lanes_log2), lds_gamma(s.lds_gamma),
         lay_k(s.lay_k), comb_k(s.comb_k), masked(s.masked), slice_vec(s.slice_vec), head_log2(s.head_log2),
-        emit_rinv(s.emit_rinv),
+        emit_rinv(s.emit_rinv), dense(s.dense), tail_lanes(s.tail_lanes),
         row_bytes(s.row_bytes), flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h),
         inv_h(s.inv_h), eps(a.eps) {}
 };
 
-// The segment's slot table, read at kernel entry with the other arguments.
+// The segment's slot table (each slot's first vector), read at kernel entry
+// with the other arguments.
 template <int VPL>
 struct Tables {
-  int lim[VPL];
   int base[VPL];
   __device__ __forceinline__ explicit Tables(const Seg& s) {
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      lim[j] = s.slot_lim[j];
-      base[j] = s.slot_base[j];
-    }
+    for (int j = 0; j < VPL; ++j) base[j] = s.slot_base[j];
     // Pin every entry here, before the dispatch on the slot count: left to
     // itself the compiler sinks the loads of entries only the wider bodies
     // use past that branch, which costs each launch a second round trip to
     // memory before its first row load. The empty asm emits nothing.
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) asm volatile("" : "+s"(lim[j]), "+s"(base[j]));
+    for (int j = 0; j < VPL; ++j) asm volatile("" : "+s"(base[j]));
   }
 };
 
@@ -353,7 +350,7 @@ struct Tables {
 template <int V>
 struct Layout {
   int wpr_log2, wpr, team, tl;
-  uint32_t off[V];  // byte offset of each slot's vector; kOutside when empty
+  uint32_t off[V];  // byte offset of each slot's vector; kOutside, or past the row, when empty
   int base[V];      // vector index of each slot, also when empty (masked layout)
 
   template <int VPL>
@@ -363,12 +360,20 @@ struct Layout {
     wpr = 1 << wpr_log2;
     team = wave >> wpr_log2;
     tl = ((wave & (wpr - 1)) << 6) | lane;  // lane within the team
-    const int sub = tl >> s.sub_lanes_log2;
+    const int stl = tl & ((1 << s.sub_lanes_log2) - 1);
+    const int lane_vec = (tl >> s.sub_lanes_log2) * s.slice_vec + stl;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      base[j] = tb.base[j] + sub * s.slice_vec + (tl & ((1 << s.sub_lanes_log2) - 1));
-      const int v = slot_vector(tb.lim[j], tb.base[j], tl, wpr_log2, s.sub_lanes_log2, s.slice_vec, s.lay_k);
-      off[j] = v >= 0 ? static_cast<uint32_t>(v) * 16u : kOutside;
+    for (int j = 0; j < V; ++j) base[j] = tb.base[j] + lane_vec;
+    // One addition per slot (the lane's offset plus the slot's base), and a
+    // lane test only on slots that end a ragged slice: this runs before the
+    // first row load.
+    if (s.dense) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) off[j] = slot_offset(tb.base[j], lane_vec, stl, false, 0, true);
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        off[j] = slot_offset(tb.base[j], lane_vec, stl, (s.flush_mask >> j) & 1u, s.tail_lanes, false);
     }
   }
 };
@@ -692,16 +697,18 @@ __device__ __forceinline__ void gamma_to_lds(const Hot& s, int wave, int lane, u
 
 // Wait for this wavefront's copies (issued before its INFLIGHT row loads, so
 // at most that many loads may stay in flight), then for the whole
-// workgroup's.
+// workgroup's. Empty slots (offsets at or past the row's end) read the last
+// weight vector: their rows are zeros and their stores are dropped.
 template <class E, int VPL, int INFLIGHT = VPL>
-__device__ __forceinline__ void gamma_from_lds(typename E::G (&g)[VPL], const Layout<VPL>& L,
+__device__ __forceinline__ void gamma_from_lds(typename E::G (&g)[VPL], const Hot& s, const Layout<VPL>& L,
                                                const u32x4* lds_g) {
+  const uint32_t last = (s.row_bytes >> 4) - 1u;
   static_assert(INFLIGHT < 64, "vmcnt holds 6 bits");
   // s_waitcnt with vmcnt = INFLIGHT and the lgkm / exp counters left alone
   __builtin_amdgcn_s_waitcnt((INFLIGHT & 0xF) | ((INFLIGHT >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) g[j] = E::gamma_lds(lds_g, L.off[j] == kOutside ? 0u : (L.off[j] >> 4));
+  for (int j = 0; j < VPL; ++j) g[j] = E::gamma_lds(lds_g, min(L.off[j] >> 4, last));
 }
 
 // Persistent workgroups: group gi, gi + G, gi + 2G, ... (G = gridDim.x). The
@@ -712,23 +719,23 @@ __device__ __forceinline__ void gamma_from_lds(typename E::G (&g)[VPL], const La
 template <class E, int VPL, bool NARROW, bool NT>
 __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L,
                                               int wave, int lane, float* part) {
-  const int G = gridDim.x;
-  int g0 = blockIdx.x;
+  const int64_t G = gridDim.x;
+  int64_t g0 = blockIdx.x;
   if (g0 >= s.nwg) return;
   u32x4 A[VPL], B[VPL];
   typename E::G g[VPL];
-  int64_t ra = static_cast<int64_t>(g0) * s.rows_per_wg + L.team;
+  int64_t ra = g0 * s.rows_per_wg + L.team;
   load_row<E, VPL, NT>(A, row_rsrc<E>(s.x, s.x_stride, ra, ra < s.T, s.row_bytes), L);
   load_gamma<E, VPL>(g, s, L);
   for (;;) {
-    const int g1 = g0 + G;
-    const int64_t rb = static_cast<int64_t>(g1) * s.rows_per_wg + L.team;
+    const int64_t g1 = g0 + G;
+    const int64_t rb = g1 * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(B, row_rsrc<E>(s.x, s.x_stride, rb, g1 < s.nwg && rb < s.T, s.row_bytes), L);
     float S = row_stat<E, VPL, NARROW>(A, s, L, wave, lane, part, true);
     scale_store<E, VPL, NT>(A, g, S, s, ra, ra < s.T, L);
     if (g1 >= s.nwg) break;
-    const int g2 = g1 + G;
-    ra = static_cast<int64_t>(g2) * s.rows_per_wg + L.team;
+    const int64_t g2 = g1 + G;
+    ra = g2 * s.rows_per_wg + L.team;
     load_row<E, VPL, NT>(A, row_rsrc<E>(s.x, s.x_stride, ra, g2 < s.nwg && ra < s.T, s.row_bytes), L);
     S = row_stat<E, VPL, NARROW>(B, s, L, wave, lane, part, true);
     scale_store<E, VPL, NT>(B, g, S, s, rb, rb < s.T, L);
@@ -744,8 +751,8 @@ __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L
 template <class E, int V, int NW, int MODE, bool NT, int RPW>
 __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int wave, int lane, float* part,
                                           u32x4* lds_g) {
-  int gi = blockIdx.x;
-  int64_t row0 = (static_cast<int64_t>(gi) * s.rows_per_wg + L.team) * RPW;
+  int64_t gi = blockIdx.x;
+  int64_t row0 = (gi * s.rows_per_wg + L.team) * RPW;
   u32x4 d[RPW][V];
   typename E::G g[V];
   const bool staged = MODE != MODE_STATS && s.lds_gamma;
@@ -755,7 +762,7 @@ __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int 
     load_row<E, V, NT>(d[r], row_rsrc<E>(s.x, s.x_stride, row0 + r, row0 + r < s.T, s.row_bytes), L);
   if constexpr (MODE != MODE_STATS) {
     if (staged)
-      gamma_from_lds<E, V, V * RPW>(g, L, lds_g);
+      gamma_from_lds<E, V, V * RPW>(g, s, L, lds_g);
     else
       load_gamma<E, V>(g, s, L);
   }
@@ -775,7 +782,7 @@ __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int 
   }
   // grids capped at the hardware limit only
   for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
-    row0 = (static_cast<int64_t>(gi) * s.rows_per_wg + L.team) * RPW;
+    row0 = (gi * s.rows_per_wg + L.team) * RPW;
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
       load_row<E, V, NT>(d[r], row_rsrc<E>(s.x, s.x_stride, row0 + r, row0 + r < s.T, s.row_bytes), L);
@@ -794,15 +801,15 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
     static_assert(!NARROW && !PIPE && MODE != MODE_HEAD, "several rows per wavefront: wavefront sub-teams only");
     body_rows<E, V, NW, MODE, NT, RPW>(s, L, wave, lane, part, lds_g);
   } else if constexpr (MODE == MODE_HEAD) {
-    int gi = blockIdx.x;
-    int64_t row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
+    int64_t gi = blockIdx.x;
+    int64_t row = gi * s.rows_per_wg + L.team;
     u32x4 d[V];
     load_row<E, V, NT>(d, row_rsrc<E>(s.x, s.x_stride, row, row < s.T, s.row_bytes), L);
     const typename E::G g = E::load_gamma(rsrc(s.gamma, (16u << s.head_log2) * E::kGammaScale),
                                           static_cast<uint32_t>(lane & ((1 << s.head_log2) - 1)) * 16u);
     head_finish<E, V, NT>(d, g, s, L, row, row < s.T, lane);
     for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
-      row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
+      row = gi * s.rows_per_wg + L.team;
       u32x4 d2[V];
       load_row<E, V, NT>(d2, row_rsrc<E>(s.x, s.x_stride, row, row < s.T, s.row_bytes), L);
       head_finish<E, V, NT>(d2, g, s, L, row, row < s.T, lane);
@@ -811,9 +818,12 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
     fwd_pipelined<E, V, NARROW, NT>(s, L, wave, lane, part);
   } else {
     // The first group needs no bounds check (a group past the end holds only
-    // empty rows), so its loads follow the argument loads directly.
-    int gi = blockIdx.x;
-    int64_t row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
+    // empty rows), so its loads follow the argument loads directly. Group
+    // indices are 64-bit in every body: with up to 2^31 - 1 rows, one
+    // workgroup per row and a grid capped at the hardware limit, a
+    // grid-stride step passes 2^31.
+    int64_t gi = blockIdx.x;
+    int64_t row = gi * s.rows_per_wg + L.team;
     bool live = row < s.T;
     u32x4 d[V];
     typename E::G g[V];
@@ -822,24 +832,24 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
     load_row<E, V, NT>(d, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
     if constexpr (MODE != MODE_STATS) {
       if (staged)
-        gamma_from_lds<E, V>(g, L, lds_g);
+        gamma_from_lds<E, V>(g, s, L, lds_g);
       else
         load_gamma<E, V>(g, s, L);
     }
     row_finish<E, V, MODE, NARROW, NT>(d, g, s, L, row, live, wave, lane, part,
-                                       gi + static_cast<int>(gridDim.x) < s.nwg);
+                                       gi + static_cast<int64_t>(gridDim.x) < s.nwg);
     // Only grids capped at the hardware limit get here. Reloading gamma each
     // time keeps the first row's registers free of this loop (holding them
     // across it costs about 40 VGPRs).
     for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
-      row = static_cast<int64_t>(gi) * s.rows_per_wg + L.team;
+      row = gi * s.rows_per_wg + L.team;
       live = row < s.T;
       u32x4 d2[V];
       typename E::G g2[V];
       load_row<E, V, NT>(d2, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
       if constexpr (MODE != MODE_STATS) load_gamma<E, V>(g2, s, L);
       row_finish<E, V, MODE, NARROW, NT>(d2, g2, s, L, row, live, wave, lane, part,
-                                         gi + static_cast<int>(gridDim.x) < s.nwg);
+                                         gi + static_cast<int64_t>(gridDim.x) < s.nwg);
     }
   }
 }

@@ -74,6 +74,8 @@ struct Seg {
   float inv_h;            // 1 / h, rounded once (exact for HEAD's power-of-two heads)
   int32_t emit_rinv;      // STATS: write 1 / sqrt(S / h + eps) instead of S
   int32_t rpw;            // rows each one-wavefront team takes at once (1, 2, 4)
+  int32_t dense;          // 1: no slot needs a lane test (see slot_offset)
+  int32_t tail_lanes;     // lanes of the last slot of each slice (the ragged slot when not dense)
   int32_t slot_base[kMaxSlots];
   int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
 };
@@ -93,6 +95,29 @@ __host__ __device__ inline int slot_vector(int lim_word, int base, int tl, int w
   const int stl = tl & ((1 << sub_lanes_log2) - 1);  // lane within the sub-team
   const int slice = sub + ((lim_word >> 16) << (6 + wpr_log2 - sub_lanes_log2));
   return (stl < (lim_word & 0xffff) && slice < K) ? base + sub * slice_vec + stl : -1;
+}
+
+// Byte offset the kernels' raw buffer accesses use for an empty slot: past
+// any row, so the hardware range check reads zeros and drops the store.
+constexpr uint32_t kOutsideOffset = 0x80000000u;
+
+// The byte offset of slot j's vector for a lane, as the kernels form it:
+// `lane_vec` = sub * slice_vec + stl is the lane's vector within its
+// sub-team's first slice (computed once per wavefront) and `base` the
+// slot's table entry. The result is 16 * slot_vector() when that vector
+// exists; otherwise it is kOutsideOffset, or lies at or past the end of the
+// row, where the range check drops the access as well: a sub-team with no
+// slice in the slot's round (slice >= K) would start at vector
+// K * slice_vec, the row's length. Within a slice every slot but the last
+// covers the whole sub-team, and the last one (`ends_slice`, its flush bit)
+// covers `tail_lanes` lanes, the same for every slice; lanes past that would
+// reach into the next slice, so only such ragged slots need the lane test.
+// When a segment has none (`dense`: one slice, the masked layout, or slices
+// that are whole multiples of the sub-team), every slot is one addition.
+__host__ __device__ inline uint32_t slot_offset(int base, int lane_vec, int stl, bool ends_slice, int tail_lanes,
+                                                bool dense) {
+  return (dense || !ends_slice || stl < tail_lanes) ? static_cast<uint32_t>(base + lane_vec) * 16u
+                                                    : kOutsideOffset;
 }
 
 // Compile-time variants a launch picks from.

@@ -34,6 +34,7 @@ hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes
 
 static int failures = 0;
 static long g_layouts[3];  // segments laid out with whole-wavefront sub-teams, narrower ones, masked
+static long g_dense;       // segments whose slots need no lane test
 #define CHECK(c, ...)                          \
   do {                                         \
     if (!(c)) {                                \
@@ -69,6 +70,15 @@ static void check_seg(const qkn::Seg& s, int nw, int vpl, int64_t nvec, int K, b
     const int sub = tl >> m;
     for (int j = 0; j < s.nslot; ++j) {
       const int v = qkn::slot_vector(s.slot_lim[j], s.slot_base[j], tl, wl, m, s.slice_vec, s.lay_k);
+      // the kernels' offset: the same vector, or an access the range check drops
+      const int stl = tl & ((1 << m) - 1);
+      const uint32_t off = qkn::slot_offset(s.slot_base[j], sub * s.slice_vec + stl, stl, (s.flush_mask >> j) & 1u,
+                                            s.tail_lanes, s.dense);
+      if (v >= 0)
+        CHECK(off == static_cast<uint32_t>(v) * 16u, "%s slot %d lane %d offset %u for vector %d", what, j, tl, off, v);
+      else
+        CHECK(off >= s.row_bytes, "%s slot %d lane %d empty but offset %u < row bytes %u", what, j, tl, off,
+              s.row_bytes);
       if (v < 0) continue;
       CHECK(v < nvec, "%s vector %d >= %lld", what, v, (long long)nvec);
       if (v >= nvec) continue;
@@ -171,6 +181,7 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
   for (int i = 0; i < nseg; ++i) {
     check_seg(seg[i], nw, vpl, in[i].nvec, K, masked[i], what);
     ++g_layouts[masked[i] ? 2 : seg[i].sub_lanes_log2 < 6 ? 1 : 0];
+    g_dense += seg[i].dense;
   }
 }
 
@@ -305,8 +316,8 @@ int main() {
   print_plan("c4f8 K=1", QKNORM_FP8_E4M3, 2048, 5120, 1024, 1);
   print_plan("c5f8 K=8", QKNORM_FP8_E4M3, 16384, 4096, 4096, 8);
   print_plan("c5f8 K=1", QKNORM_FP8_E4M3, 16384, 4096, 4096, 1);
-  std::printf("segments: %ld whole-wavefront sub-teams, %ld narrower sub-teams, %ld masked\n", g_layouts[0],
-              g_layouts[1], g_layouts[2]);
+  std::printf("segments: %ld whole-wavefront sub-teams, %ld narrower sub-teams, %ld masked; %ld dense\n",
+              g_layouts[0], g_layouts[1], g_layouts[2], g_dense);
   std::printf("%d cases, %d failures\n", cases, failures);
   return failures ? 1 : 0;
 }

@@ -323,7 +323,56 @@ def test_no_device_means_loud_failure():
         pytest.skip("a GPU is present")
     h = ctypes.c_void_p()
     assert qk.lib().qknorm_create(ctypes.byref(h), 0) == qk.ERR_DEVICE
-    x = torch.zeros(4, 256)
     with pytest.raises(qk.QKNormError) as e:
-        qk.forward(x, x, torch.ones(256), torch.ones(256))
+        qk.Context(0)
     assert e.value.status == qk.ERR_DEVICE
+    x = torch.zeros(4, 256)
+    with pytest.raises(ValueError, match="GPU"):
+        qk.forward(x, x, torch.ones(256), torch.ones(256))
+
+
+def test_binding_checks_what_the_c_abi_cannot_see():
+    """The C ABI takes bare pointers, so the binding checks sizes and types
+    of the caller's outputs and weights before any call: a too-small or
+    differently typed output, or a short weight vector, would be written or
+    read past its end. CPU tensors pass these checks and then fail the
+    device check, so no case here reaches the library."""
+    import torch
+    bf = torch.bfloat16
+    q, k = torch.zeros(8, 256, dtype=bf), torch.zeros(8, 64, dtype=bf)
+    gq, gk = torch.ones(256, dtype=bf), torch.ones(64, dtype=bf)
+    for kw, msg in [
+        (dict(out_q=torch.zeros(1, 256, dtype=bf)), "shape"),          # one row for T rows
+        (dict(out_k=torch.zeros(8, 32, dtype=bf)), "shape"),
+        (dict(out_q=torch.zeros(8, 256, dtype=torch.float32)), "dtype"),
+        (dict(gamma_q=torch.ones(128, dtype=bf)), "weights"),          # short weights
+        (dict(gamma_k=torch.ones(64, dtype=torch.float32)), "weights"),
+        (dict(), "GPU"),                                               # all valid, but host memory
+    ]:
+        args = dict(gamma_q=gq, gamma_k=gk)
+        args.update(kw)
+        with pytest.raises(ValueError, match=msg):
+            qk.forward(q, k, args.pop("gamma_q"), args.pop("gamma_k"), **args)
+    with pytest.raises(ValueError, match="shape"):
+        qk.forward_headwise(q, k, torch.ones(64, dtype=bf), torch.ones(64, dtype=bf), 64,
+                            out_q=torch.zeros(4, 256, dtype=bf))
+    with pytest.raises(ValueError, match="weights"):
+        qk.forward_headwise(q, k, torch.ones(32, dtype=bf), torch.ones(64, dtype=bf), 64)
+    with pytest.raises(ValueError, match="float32"):
+        qk.inv_rms(q, k, out_q=torch.zeros(4, dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU"):
+        qk.inv_rms(q, k)
+    xs = q[:, :64]
+    st = torch.zeros(4, 8, dtype=torch.float32)
+    with pytest.raises(ValueError, match="stats"):
+        qk.partial_stats(xs, 0, 4, stats=torch.zeros(4, 4, dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU"):
+        qk.partial_stats(xs, 0, 4, stats=st)
+    with pytest.raises(ValueError, match="64 weights"):
+        qk.apply_stats(xs, torch.ones(32, dtype=bf), st, 256)     # short gamma_slice
+    with pytest.raises(ValueError, match="shape"):
+        qk.apply_stats(xs, torch.ones(64, dtype=bf), st, 256, out=torch.zeros(8, 32, dtype=bf))
+    with pytest.raises(ValueError, match="stats"):
+        qk.apply_stats(xs, torch.ones(64, dtype=bf), torch.zeros(4, 7, dtype=torch.float32), 256)
+    with pytest.raises(ValueError, match="GPU"):
+        qk.apply_stats(xs, torch.ones(64, dtype=bf), st, 256)
