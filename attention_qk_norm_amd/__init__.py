@@ -18,6 +18,8 @@ The other entry points:
     inv_rms(q, k)                                           the per-token 1 / RMS alone
     partial_stats(x_slice, slice_index, num_slices)         split path, step 1
     apply_stats(x_slice, gamma_slice, stats, h_total)       split path, step 2
+    partial_stats_qk / apply_stats_qk                       both steps for a query and a
+                                                            key slice in one launch each
 
 Rows are float32, bfloat16 or float8_e4m3fn (with bfloat16 weights); q and
 k may be strided views, such as the column blocks of a packed QKV tensor.
@@ -37,7 +39,8 @@ ERR_NULL, ERR_SHAPE, ERR_SLICES, ERR_ALIGN, ERR_DTYPE, ERR_EPS, ERR_ALIAS, ERR_D
 # Every symbol include/qknorm.h declares.
 EXPORTS = ("qknorm_create", "qknorm_create_ex", "qknorm_destroy", "qknorm_forward",
            "qknorm_forward_headwise", "qknorm_inv_rms", "qknorm_partial_stats",
-           "qknorm_apply_stats", "qknorm_status_string", "qknorm_max_width")
+           "qknorm_apply_stats", "qknorm_partial_stats_qk", "qknorm_apply_stats_qk",
+           "qknorm_status_string", "qknorm_max_width")
 
 
 class Rows(ctypes.Structure):
@@ -85,13 +88,17 @@ def lib():
             L.qknorm_partial_stats.argtypes = [vp, ci, i64, vp, i64, i64, ci, ci, vp, vp]
             L.qknorm_apply_stats.argtypes = [vp, ci, i64, ctypes.POINTER(Rows), vp, vp, ci, i64,
                                              cf, vp]
+            L.qknorm_partial_stats_qk.argtypes = [vp, ci, i64, ctypes.POINTER(Rows), ctypes.POINTER(Rows),
+                                                  ci, ci, vp, vp, vp]
+            L.qknorm_apply_stats_qk.argtypes = [vp, ci, i64, ctypes.POINTER(Rows), ctypes.POINTER(Rows),
+                                                vp, vp, vp, vp, ci, i64, i64, cf, vp]
             L.qknorm_status_string.argtypes = [ci]
             L.qknorm_status_string.restype = ctypes.c_char_p
             L.qknorm_max_width.argtypes = [ci]
             L.qknorm_max_width.restype = i64
             for name in ("qknorm_create", "qknorm_create_ex", "qknorm_destroy", "qknorm_forward",
                          "qknorm_forward_headwise", "qknorm_inv_rms", "qknorm_partial_stats",
-                         "qknorm_apply_stats"):
+                         "qknorm_apply_stats", "qknorm_partial_stats_qk", "qknorm_apply_stats_qk"):
                 getattr(L, name).restype = ci
             _lib = L
         return _lib
@@ -346,3 +353,64 @@ def apply_stats(x_slice, gamma_slice, stats, h_total, eps=1e-6, out=None, ctx=No
                                   _stream_of(x_slice, stream))
     _check(st, "qknorm_apply_stats")
     return out
+
+
+def _stats_out(st, x, num_slices):
+    torch = _torch()
+    T = x.shape[0]
+    if st is None:
+        st = torch.zeros((num_slices, T), dtype=torch.float32, device=x.device)
+    if st.dtype != torch.float32 or st.shape != (num_slices, T) or not st.is_contiguous():
+        raise ValueError("stats must be a contiguous float32 [num_slices, T] tensor")
+    return st
+
+
+def partial_stats_qk(q_slice, k_slice, slice_index, num_slices, stats_q=None, stats_k=None, ctx=None,
+                     stream=None):
+    """partial_stats of a query slice and a key slice of the same T tokens in
+    one launch (k_slice may be None). Returns (stats_q, stats_k)."""
+    dt = _dtype_code(q_slice)
+    T = q_slice.shape[0]
+    rq = _rows_of(q_slice, None)
+    rk = None
+    if k_slice is not None:
+        if k_slice.shape[0] != T or k_slice.dtype != q_slice.dtype:
+            raise ValueError("q_slice and k_slice must share T and dtype")
+        rk = _rows_of(k_slice, None)
+    stats_q = _stats_out(stats_q, q_slice, num_slices)
+    stats_k = _stats_out(stats_k, k_slice, num_slices) if k_slice is not None else None
+    _on_one_gpu(q_slice, k_slice, stats_q, stats_k)
+    c = _ctx_of(q_slice, ctx)
+    st = lib().qknorm_partial_stats_qk(c.handle, dt, T, ctypes.byref(rq),
+                                       ctypes.byref(rk) if rk is not None else None,
+                                       int(slice_index), int(num_slices), stats_q.data_ptr(),
+                                       stats_k.data_ptr() if stats_k is not None else None,
+                                       _stream_of(q_slice, stream))
+    _check(st, "qknorm_partial_stats_qk")
+    return stats_q, stats_k
+
+
+def apply_stats_qk(q_slice, k_slice, gamma_q_slice, gamma_k_slice, stats_q, stats_k, hq_total, hk_total,
+                   eps=1e-6, out_q=None, out_k=None, ctx=None, stream=None):
+    """apply_stats of a query slice and a key slice of the same T tokens in
+    one launch (k_slice may be None; out_*=x_slice: in place). Returns
+    (y_q, y_k)."""
+    torch = _torch()
+    dt, T, rq, rk, out_q, out_k = _qk_rows(q_slice, k_slice, gamma_q_slice, gamma_k_slice,
+                                           lambda x: x.shape[1], out_q, out_k)
+    K = stats_q.shape[0] if stats_q.dim() == 2 else -1
+    for st_, x in ((stats_q, q_slice), (stats_k, k_slice)):
+        if x is None:
+            continue
+        if st_.dtype != torch.float32 or st_.dim() != 2 or st_.shape != (K, T) or not st_.is_contiguous():
+            raise ValueError("stats must be contiguous float32 [K, T] tensors of one K")
+    _on_one_gpu(q_slice, stats_q, stats_k if k_slice is not None else None)
+    c = _ctx_of(q_slice, ctx)
+    st = lib().qknorm_apply_stats_qk(c.handle, dt, T, ctypes.byref(rq), ctypes.byref(rk) if rk is not None else None,
+                                     gamma_q_slice.data_ptr(),
+                                     gamma_k_slice.data_ptr() if k_slice is not None else None,
+                                     stats_q.data_ptr(), stats_k.data_ptr() if k_slice is not None else None,
+                                     K, int(hq_total), int(hk_total) if k_slice is not None else 0, float(eps),
+                                     _stream_of(q_slice, stream))
+    _check(st, "qknorm_apply_stats_qk")
+    return out_q, out_k

@@ -1,6 +1,9 @@
-"""Build libqknorm.so in-tree for gfx950 with hipcc.
+"""Build libqknorm.so (the QK-Norm library) and libqkceil.so (the
+measurement kernels the benchmark times beside it) in-tree for gfx950 with
+hipcc.
 
-The shared object lands next to this file, where the Python binding loads it.
+The shared objects land next to this file, where the Python binding and the
+benchmark load them.
 """
 import os
 import subprocess
@@ -13,6 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqknorm.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("qknorm_kernels_f32.hip", "qknorm_kernels_bf16.hip",
                                             "qknorm_kernels_fp8.hip", "qknorm_launch.cpp", "qknorm_api.cpp")]
+CEIL_LIB = os.path.join(PKG, "libqkceil.so")
+CEIL_SOURCES = [os.path.join(CSRC, "qkceil.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -29,14 +34,15 @@ FLAGS = [
 ]
 
 
-def build(out=LIB, extra=(), verbose=False):
+def build(out=LIB, extra=(), verbose=False, sources=None):
     """Compile every HIP source (always, in parallel: one object per source)
     and link them into `out`."""
+    sources = SOURCES if sources is None else sources
     tag = "%s.tmp%d" % (out, os.getpid())
-    objs = [tag + ".%d.o" % i for i in range(len(SOURCES))]
+    objs = [tag + ".%d.o" % i for i in range(len(sources))]
     procs = []
     try:
-        for src, obj in zip(SOURCES, objs):
+        for src, obj in zip(sources, objs):
             cmd = [HIPCC, *FLAGS, *extra, "-c", "-x", "hip", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
@@ -60,5 +66,11 @@ def build(out=LIB, extra=(), verbose=False):
     return out
 
 
+def build_ceiling(verbose=False):
+    """The measurement kernels (include/qkceil.h) as libqkceil.so."""
+    return build(out=CEIL_LIB, verbose=verbose, sources=CEIL_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_ceiling(verbose="-v" in sys.argv))

@@ -720,83 +720,138 @@ int qknorm_partial_stats(qknorm_ctx* ctx, int dtype, int64_t T, const void* x_sl
   if (!valid_dtype(dtype)) return QKNORM_ERR_DTYPE;
   if (T < 0 || T > kMaxRows) return QKNORM_ERR_SHAPE;
   if (T == 0) return QKNORM_OK;
-  if (x_slice == nullptr || stats == nullptr) return QKNORM_ERR_NULL;
+  if (x_slice == nullptr) return QKNORM_ERR_NULL;
   const qknorm_rows r{x_slice, nullptr, slice_width, x_stride, slice_width};
-  int st = check_rows(&r, nullptr, dtype, false, false);
-  if (st != QKNORM_OK) return st;
-  if (slice_width > qknorm_max_width(dtype)) return QKNORM_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(stats) & 3u) != 0) return QKNORM_ERR_ALIGN;
+  return qknorm_partial_stats_qk(ctx, dtype, T, &r, nullptr, slice_index, num_slices, stats, nullptr, stream);
+}
+
+int qknorm_partial_stats_qk(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q_slice,
+                            const qknorm_rows* k_slice, int slice_index, int num_slices, float* stats_q,
+                            float* stats_k, void* stream) {
+  if (!valid_dtype(dtype)) return QKNORM_ERR_DTYPE;
+  if (T < 0 || T > kMaxRows) return QKNORM_ERR_SHAPE;
+  if (T == 0) return QKNORM_OK;
+  const qknorm_rows* segs[2] = {q_slice, k_slice};
+  float* outs[2] = {stats_q, stats_k};
+  const int nseg = k_slice != nullptr ? 2 : 1;
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i] == nullptr || outs[i] == nullptr) return QKNORM_ERR_NULL;
+    const int st = check_rows(segs[i], nullptr, dtype, false, false);
+    if (st != QKNORM_OK) return st;
+    if (segs[i]->width > qknorm_max_width(dtype)) return QKNORM_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(outs[i]) & 3u) != 0) return QKNORM_ERR_ALIGN;
+  }
   if (num_slices < 1 || num_slices > kMaxSlices || slice_index < 0 || slice_index >= num_slices)
     return QKNORM_ERR_SLICES;
-  float* out = stats + static_cast<int64_t>(slice_index) * T;
-  if (overlap(flat(out, T * 4), in_rows(r, dtype, T))) return QKNORM_ERR_ALIAS;
-  st = check_ctx(ctx);
+  float* rows_out[2] = {nullptr, nullptr};
+  for (int i = 0; i < nseg; ++i) rows_out[i] = outs[i] + static_cast<int64_t>(slice_index) * T;
+  for (int i = 0; i < nseg; ++i) {
+    const Rows oi = flat(rows_out[i], T * 4);
+    for (int j = 0; j < nseg; ++j) {
+      if (overlap(oi, in_rows(*segs[j], dtype, T))) return QKNORM_ERR_ALIAS;
+      if (j != i && overlap(oi, flat(rows_out[j], T * 4))) return QKNORM_ERR_ALIAS;
+    }
+  }
+  int st = check_ctx(ctx);
   if (st != QKNORM_OK) return st;
 
-  const int64_t nvec = slice_width / vec_elems(dtype);
-  const SegIn in{nvec, 1};
-  Plan plan;
+  const int64_t ve = vec_elems(dtype);
+  SegIn in[2];
+  for (int i = 0; i < nseg; ++i) in[i] = SegIn{segs[i]->width / ve, 1};
+  Plan plans[2];
   int nw = 4;
-  st = plan_launch(ctx, dtype, &in, 1, T, &plan, &nw);
+  st = plan_launch(ctx, dtype, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) return st;
   qkn::Args a{};
   a.T = T;
   a.eps = 0.0f;
-  qkn::Seg& s = a.seg[0];
-  s.x = x_slice;
-  s.x_stride = x_stride;
-  s.stats_out = out;
-  fill_layout(&s, plan, nw, nvec, 1, T);
-  set_width(&s, slice_width);
-  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(s.nslot, nw, dtype), nw, false, true, false};
+  int slots = 0;
+  for (int i = 0; i < nseg; ++i) {
+    qkn::Seg& s = a.seg[i];
+    s.x = segs[i]->x;
+    s.x_stride = segs[i]->x_stride;
+    s.stats_out = rows_out[i];
+    fill_layout(&s, plans[i], nw, in[i].nvec, 1, T);
+    set_width(&s, segs[i]->width);
+    slots = s.nslot > slots ? s.nslot : slots;
+  }
+  qkn::Variant v{dtype, qkn::MODE_STATS, qkn::compiled_vpl(slots, nw, dtype), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
-  return run(ctx, v, a, 1, stream);
+  return run(ctx, v, a, nseg, stream);
 }
 
 int qknorm_apply_stats(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* x_slice,
                        const void* gamma_slice, const float* stats, int num_slices, int64_t h_total,
                        float eps, void* stream) {
+  return qknorm_apply_stats_qk(ctx, dtype, T, x_slice, nullptr, gamma_slice, nullptr, stats, nullptr, num_slices,
+                               h_total, 0, eps, stream);
+}
+
+int qknorm_apply_stats_qk(qknorm_ctx* ctx, int dtype, int64_t T, const qknorm_rows* q_slice,
+                          const qknorm_rows* k_slice, const void* gamma_q_slice, const void* gamma_k_slice,
+                          const float* stats_q, const float* stats_k, int num_slices, int64_t hq_total,
+                          int64_t hk_total, float eps, void* stream) {
   if (!valid_dtype(dtype)) return QKNORM_ERR_DTYPE;
   if (T < 0 || T > kMaxRows) return QKNORM_ERR_SHAPE;
   if (T == 0) return QKNORM_OK;
-  if (stats == nullptr) return QKNORM_ERR_NULL;
-  int st = check_rows(x_slice, gamma_slice, dtype, true, true);
-  if (st != QKNORM_OK) return st;
-  if (x_slice->width > qknorm_max_width(dtype) || h_total < x_slice->width || h_total > kMaxTotalWidth)
-    return QKNORM_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(stats) & 3u) != 0) return QKNORM_ERR_ALIGN;
+  const qknorm_rows* segs[2] = {q_slice, k_slice};
+  const void* gammas[2] = {gamma_q_slice, gamma_k_slice};
+  const float* stats[2] = {stats_q, stats_k};
+  const int64_t totals[2] = {hq_total, hk_total};
+  const int nseg = k_slice != nullptr ? 2 : 1;
+  for (int i = 0; i < nseg; ++i) {
+    if (stats[i] == nullptr) return QKNORM_ERR_NULL;
+    const int st = check_rows(segs[i], gammas[i], dtype, true, true);
+    if (st != QKNORM_OK) return st;
+    if (segs[i]->width > qknorm_max_width(dtype) || totals[i] < segs[i]->width || totals[i] > kMaxTotalWidth)
+      return QKNORM_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(stats[i]) & 3u) != 0) return QKNORM_ERR_ALIGN;
+  }
   if (num_slices < 1 || num_slices > kMaxSlices) return QKNORM_ERR_SLICES;
   if (!eps_ok(eps)) return QKNORM_ERR_EPS;
-  const Rows yr = out_rows(*x_slice, dtype, T);
-  if (!in_out_ok(*x_slice, dtype, T) || overlap(yr, flat(stats, num_slices * T * 4)) ||
-      overlap(yr, flat(gamma_slice, x_slice->width * gamma_elem_bytes(dtype))))
-    return QKNORM_ERR_ALIAS;
-  st = check_ctx(ctx);
+  const int geb = gamma_elem_bytes(dtype);
+  for (int i = 0; i < nseg; ++i) {
+    if (!in_out_ok(*segs[i], dtype, T)) return QKNORM_ERR_ALIAS;
+    const Rows yi = out_rows(*segs[i], dtype, T);
+    for (int j = 0; j < nseg; ++j) {
+      if (overlap(yi, flat(stats[j], num_slices * T * 4)) || overlap(yi, flat(gammas[j], segs[j]->width * geb)))
+        return QKNORM_ERR_ALIAS;
+      if (j == i) continue;
+      if (overlap(yi, in_rows(*segs[j], dtype, T)) || overlap(yi, out_rows(*segs[j], dtype, T)))
+        return QKNORM_ERR_ALIAS;
+    }
+  }
+  int st = check_ctx(ctx);
   if (st != QKNORM_OK) return st;
 
-  const int64_t nvec = x_slice->width / vec_elems(dtype);
-  const SegIn in{nvec, 1};
-  Plan plan;
+  const int64_t ve = vec_elems(dtype);
+  SegIn in[2];
+  for (int i = 0; i < nseg; ++i) in[i] = SegIn{segs[i]->width / ve, 1};
+  Plan plans[2];
   int nw = 4;
-  st = plan_launch(ctx, dtype, &in, 1, T, &plan, &nw);
+  st = plan_launch(ctx, dtype, in, nseg, T, plans, &nw);
   if (st != QKNORM_OK) return st;
   qkn::Args a{};
   a.T = T;
   a.eps = eps;
-  qkn::Seg& s = a.seg[0];
-  s.x = x_slice->x;
-  s.y = x_slice->y;
-  s.gamma = gamma_slice;
-  s.stats_in = stats;
-  s.x_stride = x_slice->x_stride;
-  s.y_stride = x_slice->y_stride;
-  fill_layout(&s, plan, nw, nvec, 1, T);
-  share_gamma(&s, dtype);
-  s.comb_k = num_slices;
-  set_width(&s, h_total);
-  qkn::Variant v{dtype, qkn::MODE_APPLY, qkn::compiled_vpl(s.nslot, nw, dtype), nw, false, true, false};
+  int slots = 0;
+  for (int i = 0; i < nseg; ++i) {
+    qkn::Seg& s = a.seg[i];
+    s.x = segs[i]->x;
+    s.y = segs[i]->y;
+    s.gamma = gammas[i];
+    s.stats_in = stats[i];
+    s.x_stride = segs[i]->x_stride;
+    s.y_stride = segs[i]->y_stride;
+    fill_layout(&s, plans[i], nw, in[i].nvec, 1, T);
+    share_gamma(&s, dtype);
+    s.comb_k = num_slices;
+    set_width(&s, totals[i]);
+    slots = s.nslot > slots ? s.nslot : slots;
+  }
+  qkn::Variant v{dtype, qkn::MODE_APPLY, qkn::compiled_vpl(slots, nw, dtype), nw, false, true, false};
   if (v.vpl == 0) return QKNORM_ERR_SHAPE;
-  return run(ctx, v, a, 1, stream);
+  return run(ctx, v, a, nseg, stream);
 }
 
 }  // extern "C"

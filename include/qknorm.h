@@ -247,6 +247,55 @@ int qknorm_apply_stats(qknorm_ctx *ctx, int dtype, int64_t T,
                        const float *stats, int num_slices, int64_t h_total,
                        float eps, void *stream);
 
+/*
+ * Split path, step 1, for the query slice and the key slice of the same
+ * tokens in one launch: qknorm_partial_stats applied to each (Algorithm 1,
+ * Phase A, for the two normalisations a layer makes; a rank publishes both
+ * tensors' partials in one exchange).
+ *
+ *   q_slice, k_slice  the slices' rows: x, width (the slice width) and
+ *                     x_stride are read, y is ignored; k_slice may be NULL
+ *   slice_index, num_slices  as for qknorm_partial_stats, the same for both
+ *   stats_q, stats_k  fp32 device arrays laid out [num_slices][T]; the call
+ *                     writes row slice_index of each and touches nothing
+ *                     else (stats_k is ignored when k_slice is NULL)
+ * Status, in validation order: QKNORM_ERR_DTYPE, QKNORM_ERR_SHAPE (T < 0;
+ * T == 0 returns QKNORM_OK), then for q and k in turn QKNORM_ERR_NULL,
+ * QKNORM_ERR_SHAPE, QKNORM_ERR_ALIGN (the statistics need 4-byte alignment),
+ * then QKNORM_ERR_SLICES, QKNORM_ERR_ALIAS (a written statistics row
+ * overlaps the rows or the other one), QKNORM_ERR_CONTEXT, QKNORM_ERR_DEVICE.
+ */
+int qknorm_partial_stats_qk(qknorm_ctx *ctx, int dtype, int64_t T,
+                            const qknorm_rows *q_slice, const qknorm_rows *k_slice,
+                            int slice_index, int num_slices,
+                            float *stats_q, float *stats_k, void *stream);
+
+/*
+ * Split path, step 2, for the query slice and the key slice of the same
+ * tokens in one launch: qknorm_apply_stats applied to each (Algorithm 1,
+ * Phase B's scalar sum and inverse RMS, then Phase C; review Eqs. 5-8).
+ *
+ *   q_slice, k_slice  the slices' rows, output to y (may equal x); k_slice
+ *                     may be NULL
+ *   gamma_q_slice, gamma_k_slice  the weights of those columns
+ *   stats_q, stats_k  fp32 [num_slices][T] partial sums of each tensor
+ *   hq_total, hk_total  widths of the FULL query and key rows (the means
+ *                     divide by them)
+ *   num_slices, eps, stream: as for qknorm_apply_stats
+ * Status, in validation order: QKNORM_ERR_DTYPE, QKNORM_ERR_SHAPE (T < 0;
+ * T == 0 returns QKNORM_OK), then for q and k in turn QKNORM_ERR_NULL,
+ * QKNORM_ERR_SHAPE (including h_total < width or h_total > 2^24),
+ * QKNORM_ERR_ALIGN, then QKNORM_ERR_SLICES (num_slices outside [1, 64]),
+ * QKNORM_ERR_EPS, QKNORM_ERR_ALIAS (an output overlaps an input of either
+ * tensor, without being that same input, or the other output),
+ * QKNORM_ERR_CONTEXT, QKNORM_ERR_DEVICE.
+ */
+int qknorm_apply_stats_qk(qknorm_ctx *ctx, int dtype, int64_t T,
+                          const qknorm_rows *q_slice, const qknorm_rows *k_slice,
+                          const void *gamma_q_slice, const void *gamma_k_slice,
+                          const float *stats_q, const float *stats_k, int num_slices,
+                          int64_t hq_total, int64_t hk_total, float eps, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *qknorm_status_string(int status);
 

@@ -305,6 +305,73 @@ def test_apply_stats_validation(L):
         assert _apply(L, **kw) == want, kw
 
 
+def _stats_qk(L, dtype=qk.BF16, T=256, q="default", k="default", s=1, K=4, sq=A + 64 * MB, sk=A + 65 * MB):
+    # slice 1 of 4 of a packed [T, 5120 + 1024] buffer: query columns 1280-2559, key columns 5376-5631
+    if q == "default":
+        q = qk.Rows(A + 2 * 1280, None, 1280, 6144, 1280)
+    if k == "default":
+        k = qk.Rows(A + 2 * (5120 + 256), None, 256, 6144, 256)
+    return L.qknorm_partial_stats_qk(None, dtype, T, ctypes.byref(q) if q is not None else None,
+                                     ctypes.byref(k) if k is not None else None, s, K, sq, sk, None)
+
+
+def test_partial_stats_qk_validation(L):
+    R = qk.Rows
+    assert _stats_qk(L) == qk.ERR_CONTEXT
+    assert _stats_qk(L, k=None) == qk.ERR_CONTEXT
+    assert _stats_qk(L, k=None, sk=None) == qk.ERR_CONTEXT  # stats_k unused without k
+    assert _stats_qk(L, T=0) == qk.OK
+    for kw, want in [
+        (dict(dtype=9), qk.ERR_DTYPE), (dict(T=-3), qk.ERR_SHAPE),
+        (dict(q=None), qk.ERR_NULL), (dict(sq=None), qk.ERR_NULL), (dict(sk=None), qk.ERR_NULL),
+        (dict(q=R(None, None, 1280, 6144, 1280)), qk.ERR_NULL),
+        (dict(q=R(A, None, 0, 6144, 0)), qk.ERR_SHAPE), (dict(k=R(A, None, 256, 100, 256)), qk.ERR_SHAPE),
+        (dict(k=R(A + 8, None, 256, 6144, 256)), qk.ERR_ALIGN), (dict(sk=A + 65 * MB + 2), qk.ERR_ALIGN),
+        (dict(k=R(A, None, 252, 6144, 252)), qk.ERR_ALIGN),
+        (dict(s=4), qk.ERR_SLICES), (dict(s=-1), qk.ERR_SLICES), (dict(K=0), qk.ERR_SLICES),
+        (dict(sq=A + 2 * 1280 + 100 - 256 * 4), qk.ERR_ALIAS),  # row 1 of stats_q over the rows
+        (dict(sk=A + 64 * MB), qk.ERR_ALIAS),               # the two written rows coincide
+    ]:
+        assert _stats_qk(L, **kw) == want, kw
+    # different rows of one [2][K][T] block are fine
+    assert _stats_qk(L, sk=A + 64 * MB + 4 * 256 * 4) == qk.ERR_CONTEXT
+
+
+def _apply_qk(L, dtype=qk.BF16, T=256, q="default", k="default", gq=A + 60 * MB, gk=A + 61 * MB,
+              sq=A + 64 * MB, sk=A + 65 * MB, K=4, hq=5120, hk=1024, eps=1e-6):
+    if q == "default":
+        q = qk.Rows(A, A + 8 * MB, 1280, 5120, 1280)
+    if k == "default":
+        k = qk.Rows(A + 16 * MB, A + 24 * MB, 256, 1024, 256)
+    return L.qknorm_apply_stats_qk(None, dtype, T, ctypes.byref(q) if q is not None else None,
+                                   ctypes.byref(k) if k is not None else None, gq, gk, sq, sk, K, hq, hk,
+                                   eps, None)
+
+
+def test_apply_stats_qk_validation(L):
+    R = qk.Rows
+    assert _apply_qk(L) == qk.ERR_CONTEXT
+    assert _apply_qk(L, k=None, gk=None, sk=None) == qk.ERR_CONTEXT
+    assert _apply_qk(L, q=R(A, A, 1280, 5120, 5120), k=R(A + 16 * MB, A + 16 * MB, 256, 1024, 1024)) == \
+        qk.ERR_CONTEXT  # both in place
+    assert _apply_qk(L, T=0) == qk.OK
+    for kw, want in [
+        (dict(dtype=-1), qk.ERR_DTYPE), (dict(T=-1), qk.ERR_SHAPE),
+        (dict(q=None), qk.ERR_NULL), (dict(sq=None), qk.ERR_NULL), (dict(sk=None), qk.ERR_NULL),
+        (dict(gk=None), qk.ERR_NULL), (dict(k=R(A + 16 * MB, None, 256, 1024, 256)), qk.ERR_NULL),
+        (dict(hq=1000), qk.ERR_SHAPE), (dict(hk=128), qk.ERR_SHAPE), (dict(hk=(1 << 24) + 8), qk.ERR_SHAPE),
+        (dict(sk=A + 65 * MB + 1), qk.ERR_ALIGN), (dict(gk=A + 61 * MB + 8), qk.ERR_ALIGN),
+        (dict(K=0), qk.ERR_SLICES), (dict(K=65), qk.ERR_SLICES),
+        (dict(eps=float("nan")), qk.ERR_EPS),
+        (dict(k=R(A + 16 * MB, A + 65 * MB, 256, 1024, 256)), qk.ERR_ALIAS),   # y_k over stats_k
+        (dict(k=R(A + 16 * MB, A + 64 * MB, 256, 1024, 256)), qk.ERR_ALIAS),   # y_k over stats_q
+        (dict(k=R(A + 16 * MB, A + 60 * MB, 256, 1024, 256)), qk.ERR_ALIAS),   # y_k over gamma_q
+        (dict(k=R(A + 16 * MB, A + 1024, 256, 1024, 256)), qk.ERR_ALIAS),      # y_k over x_q
+        (dict(k=R(A + 16 * MB, A + 8 * MB, 256, 1024, 256)), qk.ERR_ALIAS),    # y_k over y_q
+    ]:
+        assert _apply_qk(L, **kw) == want, kw
+
+
 def test_create_validation(L):
     h = ctypes.c_void_p()
     assert L.qknorm_create(None, 0) == qk.ERR_NULL

@@ -654,6 +654,105 @@ def test_split_path_on_a_rank_slice():
         assert_parity(ys, ref[:, s * w:(s + 1) * w], torch.bfloat16, "slice %d" % s)
 
 
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_split_path_qk_on_rank_shards(name):
+    """The two-tensor split calls on what a tensor-parallel rank holds: its
+    own contiguous [T, H/K] shards of q and of k (Algorithm 1's X_local).
+    Each rank publishes both tensors' partials in one launch, then
+    normalises both shards in one launch with all K partials; the result is
+    the oracle's, and bit for bit what the single-tensor calls give on
+    strided column views of the full rows."""
+    d = workloads.generate(name)
+    w = d["w"]
+    K = w.slices[0]
+    T = min(w.T, 4096)
+    q, k = d["q"][:T], d["k"][:T]
+    refq, Pq = oracle.forward(q, d["gamma_q"], w.eps, K)
+    refk, Pk = oracle.forward(k, d["gamma_k"], w.eps, K)
+    wq, wk = w.hq // K, w.hk // K
+    shards = [(gpu(q[:, r * wq:(r + 1) * wq]), gpu(k[:, r * wk:(r + 1) * wk])) for r in range(K)]
+    gq, gk = gpu(d["gamma_q"]), gpu(d["gamma_k"])
+    sq = torch.zeros((K, T), dtype=torch.float32, device=DEV)
+    sk = torch.zeros((K, T), dtype=torch.float32, device=DEV)
+    say("split qk partials", name, "T=%d K=%d shards %d/%d" % (T, K, wq, wk))
+    for r, (xq, xk) in enumerate(shards):
+        qk.partial_stats_qk(xq, xk, r, K, sq, sk)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(sq.cpu().numpy(), Pq, rtol=1e-5)
+    np.testing.assert_allclose(sk.cpu().numpy(), Pk, rtol=1e-5)
+    say("split qk apply", name)
+    outs = []
+    for r, (xq, xk) in enumerate(shards):
+        yq, yk = qk.apply_stats_qk(xq, xk, gq[r * wq:(r + 1) * wq], gk[r * wk:(r + 1) * wk], sq, sk,
+                                   w.hq, w.hk, eps=w.eps)
+        outs.append((yq, yk))
+    torch.cuda.synchronize()
+    assert_parity(torch.cat([o[0] for o in outs], 1), refq, w.torch_dtype, "split qk q")
+    assert_parity(torch.cat([o[1] for o in outs], 1), refk, w.torch_dtype, "split qk k")
+    # the single-tensor calls on strided views of the full rows give the same bits
+    say("split qk vs single-tensor calls on views", name)
+    qd, kd = gpu(q), gpu(k)
+    st1 = torch.zeros((K, T), dtype=torch.float32, device=DEV)
+    for r in range(K):
+        qk.partial_stats(qd[:, r * wq:(r + 1) * wq], r, K, st1)
+    y1 = qk.apply_stats(qd[:, wq:2 * wq], gq[wq:2 * wq], st1, w.hq, eps=w.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(st1, sq)
+    assert torch.equal(y1, outs[1][0])
+    # in place on the shards, query slice alone (k_slice None)
+    xq = shards[0][0]
+    qk.apply_stats_qk(xq, None, gq[:wq], None, sq, None, w.hq, 0, eps=w.eps, out_q=xq)
+    torch.cuda.synchronize()
+    assert torch.equal(xq, outs[0][0])
+
+
+def test_denormal_squares_of_bf16_rows():
+    """bf16 rows whose squares are denormal fp32 values: entries m * 2^-70
+    with |m| <= 3 (exact in bf16), squares m^2 * 2^-140 (exact fp32
+    denormals), row sums below 2^-126, and means (a multiple of 2^-149 for
+    these widths) that are exact fp32 denormals too. The bf16 squares go
+    through the bf16 dot-product instruction; a flush of denormal products
+    or sums would leave S = 0 and, with eps = 0, infinite outputs, where the
+    fp64 oracle is finite (review "Prerequisites", Eq. 1). Checked with
+    eps = 0 and a denormal eps = 2^-130, for the fused forward (1 and 4
+    slices), the split path, the inverse RMS and the headwise form."""
+    T, H, D = 40, 512, 128
+    rng = np.random.default_rng(101)
+    m = rng.integers(-3, 4, size=(T, H)).astype(np.float32)
+    m[:, 0] = 3.0  # no row is all zero
+    x = torch.from_numpy(m * np.float32(2.0 ** -70)).to(torch.bfloat16)
+    assert torch.equal(x.float(), torch.from_numpy(m * np.float32(2.0 ** -70)))
+    g = workloads.random_weights(H, "bf16", 102)
+    xd, gd = gpu(x), gpu(g)
+    for eps in (0.0, 2.0 ** -130):
+        for K in (1, 4):
+            say("denormal squares bf16 forward eps=%g K=%d" % (eps, K))
+            y, _ = qk.forward(xd, None, gd, None, eps=eps, num_slices=K)
+            torch.cuda.synchronize()
+            ref, P = oracle.forward(x, g, eps, K)
+            assert (P.sum(axis=0) < 2.0 ** -126).all(), "the case must reach denormal sums"
+            assert_parity(y, ref, torch.bfloat16, "denormal squares forward K=%d eps=%g" % (K, eps))
+        say("denormal squares bf16 split eps=%g" % eps)
+        K, wd = 4, H // 4
+        st = torch.zeros((K, T), dtype=torch.float32, device=DEV)
+        for s_ in range(K):
+            qk.partial_stats(xd[:, s_ * wd:(s_ + 1) * wd], s_, K, st)
+        ys = torch.empty_like(xd)
+        for s_ in range(K):
+            qk.apply_stats(xd[:, s_ * wd:(s_ + 1) * wd], gd[s_ * wd:(s_ + 1) * wd], st, H, eps,
+                           out=ys[:, s_ * wd:(s_ + 1) * wd])
+        torch.cuda.synchronize()
+        ref, P = oracle.forward(x, g, eps, K)
+        np.testing.assert_allclose(st.cpu().double().numpy(), P, rtol=1e-6)
+        assert_parity(ys, ref, torch.bfloat16, "denormal squares split eps=%g" % eps)
+        say("denormal squares bf16 inverse RMS and headwise eps=%g" % eps)
+        r, _ = qk.inv_rms(xd, eps=eps, num_slices=4)
+        yh, _ = qk.forward_headwise(xd, None, gd[:D], None, D, eps=eps)
+        torch.cuda.synchronize()
+        assert_parity(r, oracle.inv_rms(x, eps, 4), torch.float32, "denormal squares rinv eps=%g" % eps)
+        assert_parity(yh, oracle.headwise(x, g[:D], D, eps), torch.bfloat16, "denormal squares headwise")
+
+
 def test_denormal_statistics():
     """Rows whose mean of squares is a denormal fp32 value: three entries of
     +-2^-60 in 256 columns (squares 2^-120, normal and exact) and eps = 2^-130,
