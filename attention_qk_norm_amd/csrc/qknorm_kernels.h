@@ -885,71 +885,61 @@ __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   dispatch<E, VPL, VPL, NW, MODE, NARROW, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
 }
 
-// Several rows per wavefront, 4-wavefront workgroups: statistics-only
-// launches over rows of 1 or 2 slots (2 or 4 rows), and FP8 forward launches
-// of a single round of wavefronts (2 rows, up to 8 slots).
-template <class E, int VPL, int RPW>
-hipError_t launch_rows(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
-  const dim3 bd(4 * kWave);
-  if (v.mode == MODE_STATS) {
-    if constexpr (VPL <= 2) {
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, 4, MODE_STATS, false, true, false, RPW>), gd, bd, lds, st, a);
-      return hipGetLastError();
-    }
-  } else if (v.mode == MODE_FWD && v.nt) {
-    if constexpr (E::kDtype == QKNORM_FP8_E4M3 && RPW == 2) {
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, 4, MODE_FWD, false, true, false, RPW>), gd, bd, lds, st, a);
-      return hipGetLastError();
-    }
+// The launch dispatch: the run-time variant picks one of the kernels the
+// compiled() table names; any other combination instantiates nothing and is
+// refused.
+template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW>
+hipError_t launch_one(const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
+  if constexpr (compiled(E::kDtype, MODE, VPL, NW, NARROW, NT, PIPE, RPW)) {
+    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE, NARROW, NT, PIPE, RPW>), gd, dim3(NW * kWave), lds, st, a);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+}
+
+template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE>
+hipError_t by_rpw(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
+  switch (v.rpw) {
+    case 1: return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 1>(a, gd, lds, st);
+    case 2: return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 2>(a, gd, lds, st);
+    case 4: return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 4>(a, gd, lds, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT>
+hipError_t by_pipe(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
+  return v.pipe ? by_rpw<E, VPL, NW, MODE, NARROW, NT, true>(v, a, gd, lds, st)
+                : by_rpw<E, VPL, NW, MODE, NARROW, NT, false>(v, a, gd, lds, st);
+}
+
+template <class E, int VPL, int NW, int MODE, bool NARROW>
+hipError_t by_nt(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
+  return v.nt ? by_pipe<E, VPL, NW, MODE, NARROW, true>(v, a, gd, lds, st)
+              : by_pipe<E, VPL, NW, MODE, NARROW, false>(v, a, gd, lds, st);
+}
+
+template <class E, int VPL, int NW, int MODE>
+hipError_t by_narrow(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
+  return v.narrow ? by_nt<E, VPL, NW, MODE, true>(v, a, gd, lds, st)
+                  : by_nt<E, VPL, NW, MODE, false>(v, a, gd, lds, st);
 }
 
 template <class E, int VPL, int NW>
 hipError_t launch_vpl(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
-  const dim3 bd(NW * kWave);
-  if constexpr (NW == 4) {
-    if (v.rpw == 2) return launch_rows<E, VPL, 2>(v, a, gd, lds, st);
-    if constexpr (VPL <= 2) {
-      if (v.rpw == 4) return launch_rows<E, VPL, 4>(v, a, gd, lds, st);
-    }
+  switch (v.mode) {
+    case MODE_FWD: return by_narrow<E, VPL, NW, MODE_FWD>(v, a, gd, lds, st);
+    case MODE_STATS: return by_narrow<E, VPL, NW, MODE_STATS>(v, a, gd, lds, st);
+    case MODE_APPLY: return by_narrow<E, VPL, NW, MODE_APPLY>(v, a, gd, lds, st);
+    case MODE_HEAD: return by_narrow<E, VPL, NW, MODE_HEAD>(v, a, gd, lds, st);
+    default: return hipErrorInvalidValue;
   }
-  if (v.rpw != 1) return hipErrorInvalidValue;
-  if (v.mode == MODE_FWD) {
-    if constexpr (NW == 4) {
-      if (v.pipe) {
-        if (v.narrow)
-          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, true>), gd, bd, lds, st, a);
-        else if (v.nt)
-          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, true>), gd, bd, lds, st, a);
-        else
-          hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false, true>), gd, bd, lds, st, a);
-        return hipGetLastError();
-      }
-    }
-    if (v.narrow)
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, true, true, false>), gd, bd, lds, st, a);
-    else if (v.nt)
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, true, false>), gd, bd, lds, st, a);
-    else
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_FWD, false, false, false>), gd, bd, lds, st, a);
-  } else if (v.mode == MODE_HEAD) {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_HEAD, false, true, false>), gd, bd, lds, st, a);
-  } else if (v.mode == MODE_STATS) {
-    if (v.narrow)
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, true, true, false>), gd, bd, lds, st, a);
-    else
-      hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_STATS, false, true, false>), gd, bd, lds, st, a);
-  } else {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE_APPLY, false, true, false>), gd, bd, lds, st, a);
-  }
-  return hipGetLastError();
 }
 
 template <class E>
 hipError_t launch_dtype(const Variant& v, const Args& a, dim3 grid, unsigned lds, hipStream_t st) {
-  // only the slot counts the element type may use are instantiated
-  constexpr int kCap4 = max_slots(E::kDtype, 4), kCap16 = max_slots(E::kDtype, 16);
+  if (!compiled(v) || v.dtype != E::kDtype) return hipErrorInvalidValue;
   if (v.nw == 4) {
     switch (v.vpl) {
       case 1: return launch_vpl<E, 1, 4>(v, a, grid, lds, st);
@@ -960,23 +950,19 @@ hipError_t launch_dtype(const Variant& v, const Args& a, dim3 grid, unsigned lds
       case 6: return launch_vpl<E, 6, 4>(v, a, grid, lds, st);
       case 7: return launch_vpl<E, 7, 4>(v, a, grid, lds, st);
       case 8: return launch_vpl<E, 8, 4>(v, a, grid, lds, st);
-      case 10: if constexpr (kCap4 >= 10) return launch_vpl<E, 10, 4>(v, a, grid, lds, st); break;
-      case 12: if constexpr (kCap4 >= 12) return launch_vpl<E, 12, 4>(v, a, grid, lds, st); break;
-      case 16: if constexpr (kCap4 >= 16) return launch_vpl<E, 16, 4>(v, a, grid, lds, st); break;
-      default: break;
-    }
-    return hipErrorInvalidValue;
-  }
-  if (v.nw == 16) {
-    switch (v.vpl) {
-      case 1: return launch_vpl<E, 1, 16>(v, a, grid, lds, st);
-      case 2: return launch_vpl<E, 2, 16>(v, a, grid, lds, st);
-      case 4: return launch_vpl<E, 4, 16>(v, a, grid, lds, st);
-      case 8: if constexpr (kCap16 >= 8) return launch_vpl<E, 8, 16>(v, a, grid, lds, st); break;
-      default: break;
+      case 10: return launch_vpl<E, 10, 4>(v, a, grid, lds, st);
+      case 12: return launch_vpl<E, 12, 4>(v, a, grid, lds, st);
+      case 16: return launch_vpl<E, 16, 4>(v, a, grid, lds, st);
+      default: return hipErrorInvalidValue;
     }
   }
-  return hipErrorInvalidValue;
+  switch (v.vpl) {
+    case 1: return launch_vpl<E, 1, 16>(v, a, grid, lds, st);
+    case 2: return launch_vpl<E, 2, 16>(v, a, grid, lds, st);
+    case 4: return launch_vpl<E, 4, 16>(v, a, grid, lds, st);
+    case 8: return launch_vpl<E, 8, 16>(v, a, grid, lds, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace

@@ -164,6 +164,48 @@ inline int compiled_vpl(int slots, int nw, int dtype) {
   return 0;
 }
 
+// Whether a kernel is compiled for a variant: the launch dispatch
+// instantiates exactly these, and the host-side layout checker confirms
+// that every variant the planner reaches is among them (and lists any that
+// none reaches).
+//  - slot counts: those of kVpl4 / kVpl16 up to the type's register cap;
+//  - several rows per wavefront (rpw 2 or 4): 4-wavefront workgroups of
+//    whole-wavefront sub-teams, streaming, unpipelined; statistics-only
+//    passes over rows of 1 slot (4 rows) or 2 slots (2 rows), or FP8
+//    forward passes with 2 rows;
+//  - the persistent pipelined body: forward passes in 4-wavefront
+//    workgroups;
+//  - narrow-slice kernels stream (nt) and never serve the headwise form or
+//    the split path's apply step, whose layouts hold one slice;
+//  - ordinary cached row accesses (nt off): forward passes only.
+constexpr bool compiled_vpl_value(int vpl, int nw, int dtype) {
+  if (vpl < 1 || vpl > max_slots(dtype, nw)) return false;
+  if (nw == 4) {
+    for (int c : kVpl4)
+      if (c == vpl) return true;
+  } else if (nw == 16) {
+    for (int c : kVpl16)
+      if (c == vpl) return true;
+  }
+  return false;
+}
+constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool nt, bool pipe, int rpw) {
+  if (!compiled_vpl_value(vpl, nw, dtype)) return false;
+  if (rpw != 1) {
+    if (nw != 4 || narrow || !nt || pipe) return false;
+    return (mode == MODE_STATS && ((vpl == 1 && rpw == 4) || (vpl == 2 && rpw == 2))) ||
+           (mode == MODE_FWD && dtype == QKNORM_FP8_E4M3 && rpw == 2);
+  }
+  if (narrow && !nt) return false;
+  if (pipe && (mode != MODE_FWD || nw != 4)) return false;
+  if (!nt && mode != MODE_FWD) return false;
+  if (narrow && (mode == MODE_HEAD || mode == MODE_APPLY)) return false;
+  return true;
+}
+inline bool compiled(const Variant& v) {
+  return compiled(v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw);
+}
+
 // Enqueue one launch: grid.x workgroups per segment, grid.y segments, with
 // `lds_bytes` of dynamic LDS for staged gamma. Returns hipSuccess or the
 // launch error. Dispatches on v.dtype to one of the per-type entries below,

@@ -12,22 +12,57 @@
 //    copy loop's bound;
 //  - headwise plans keep every head inside one aligned lane group of one
 //    wavefront and slot, lane l holding the head's vector l mod (vectors
-//    per head).
-#include "qknorm_api.cpp"
+//    per head);
+//  - the kernels' slot offsets (slot_offset) equal the table's vectors, or
+//    fall where the buffer range check drops the access;
+//  - every public entry point, over shapes, slice counts and every
+//    combination of schedule options, asks only for variants that have a
+//    kernel (compiled()), and every compiled variant is reached by some
+//    call.
+#include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <set>
+#include <tuple>
 #include <vector>
+
+// The entry points ask HIP for the current device before launching; here
+// there is none, so the library's call is routed to this stand-in (device 0,
+// the fake contexts' device) and every entry point runs its real validation
+// and planning up to the launch, which the recorder below replaces.
+static hipError_t layout_check_hipGetDevice(int* d) {
+  *d = 0;
+  return hipSuccess;
+}
+#define hipGetDevice layout_check_hipGetDevice
+#include "qknorm_api.cpp"
+#undef hipGetDevice
 
 namespace qkn {
 static Variant g_v;
 static Args g_a;
 static dim3 g_grid;
 static unsigned g_lds;
+using VariantKey = std::tuple<int, int, int, int, bool, bool, bool, int>;
+static VariantKey key(const Variant& v) {
+  return VariantKey{v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw};
+}
+static std::set<VariantKey> g_reached;
+static long g_launches, g_uncompiled;
 hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t) {
   g_v = v;
   g_a = a;
   g_grid = grid;
   g_lds = lds_bytes;
+  g_reached.insert(key(v));
+  ++g_launches;
+  if (!compiled(v)) {
+    if (g_uncompiled < 10)
+      std::printf("FAIL no kernel for reached variant dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d\n",
+                  v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw);
+    ++g_uncompiled;
+    return hipErrorInvalidValue;
+  }
   return hipSuccess;
 }
 }  // namespace qkn
@@ -270,6 +305,60 @@ static void print_plan(const char* name, int dtype, int64_t T, int64_t hq, int64
   std::printf("\n");
 }
 
+// Every public entry point, over shapes, slice counts and schedule options,
+// through the library's own validation and planning: records each variant a
+// launch asks for. Fake device addresses, far apart, are never dereferenced.
+static long sweep_entry_points() {
+  long calls = 0;
+  const uintptr_t B = 0x100000000000ull, G = 0x1000000000ull;  // tensors 64 GiB apart
+  auto P = [&](int i) { return reinterpret_cast<void*>(B + i * G); };
+  std::vector<qknorm_options> opts;
+  for (int w : {0, 1, 2, 4, 8, 16})
+    for (int cap : {0, 3})
+      for (int cached : {0, 1}) opts.push_back(qknorm_options{w, cap, cached});
+  // every slot count of one-wavefront rows for each element type (256 fp32,
+  // 512 bf16 or 1024 fp8 columns per slot), and wider rows for the teams
+  std::vector<int64_t> widths = {8, 64, 200, 1000, 1280, 12288, 24576, 49152, 65536};
+  for (int64_t slots = 1; slots <= 32; ++slots)
+    for (int64_t per : {256, 512, 1024}) widths.push_back(slots * per);
+  const int64_t rows[] = {1, 64, 256, 2048, 16384, 100000};
+  const int ks[] = {1, 2, 4, 8, 64};
+  for (const qknorm_options& o : opts) {
+    qknorm_ctx ctx{0, 256, o};
+    for (int dtype : {QKNORM_BF16, QKNORM_F32, QKNORM_FP8_E4M3})
+      for (int64_t hq : widths)
+        for (int64_t hk : {hq, hq / 4}) {
+          const int64_t ve = vec_elems(dtype);
+          if (hq > qknorm_max_width(dtype) || hk < ve || hk % ve) continue;
+          for (int64_t T : rows) {
+            qknorm_rows q{P(0), P(1), hq, hq, hq}, k{P(2), P(3), hk, hk, hk};
+            for (int K : ks) {
+              calls += 3;
+              qknorm_forward(&ctx, dtype, T, &q, &k, P(4), P(5), 1e-6f, K, nullptr);
+              qknorm_forward(&ctx, dtype, T, &q, nullptr, P(4), nullptr, 1e-6f, K, nullptr);
+              qknorm_inv_rms(&ctx, dtype, T, &q, &k, 1e-6f, K, static_cast<float*>(P(6)),
+                             static_cast<float*>(P(7)), nullptr);
+              if (hq % K || hk % K || (hq / K) % ve || (hk / K) % ve) continue;
+              qknorm_rows qs{P(0), P(1), hq / K, hq, hq}, ks_{P(2), P(3), hk / K, hk, hk};
+              calls += 4;
+              qknorm_partial_stats_qk(&ctx, dtype, T, &qs, &ks_, 0, K, static_cast<float*>(P(6)),
+                                      static_cast<float*>(P(7)), nullptr);
+              qknorm_partial_stats(&ctx, dtype, T, P(0), hq, hq / K, 0, K, static_cast<float*>(P(6)), nullptr);
+              qknorm_apply_stats_qk(&ctx, dtype, T, &qs, &ks_, P(4), P(5), static_cast<const float*>(P(6)),
+                                    static_cast<const float*>(P(7)), K, hq, hk, 1e-6f, nullptr);
+              qknorm_apply_stats(&ctx, dtype, T, &qs, P(4), static_cast<const float*>(P(6)), K, hq, 1e-6f,
+                                 nullptr);
+            }
+            for (int64_t D = 1; D <= hk; D *= 2) {
+              ++calls;
+              qknorm_forward_headwise(&ctx, dtype, T, &q, &k, P(4), P(5), D, 1e-6f, nullptr);
+            }
+          }
+        }
+  }
+  return calls;
+}
+
 int main() {
   int cases = 0;
   const int64_t widths[] = {8, 24, 64, 96, 200, 256, 512, 1000, 1024, 1032, 1280, 1536, 2048,
@@ -318,6 +407,31 @@ int main() {
   print_plan("c5f8 K=1", QKNORM_FP8_E4M3, 16384, 4096, 4096, 1);
   std::printf("segments: %ld whole-wavefront sub-teams, %ld narrower sub-teams, %ld masked; %ld dense\n",
               g_layouts[0], g_layouts[1], g_layouts[2], g_dense);
+  // the kernels a call can ask for, and the ones compiled for none
+  const long calls = sweep_entry_points();
+  CHECK(qkn::g_uncompiled == 0, "%ld launches asked for a variant without a kernel", qkn::g_uncompiled);
+  long compiled_n = 0;
+  std::vector<qkn::VariantKey> unused;
+  for (int dtype : {QKNORM_F32, QKNORM_BF16, QKNORM_FP8_E4M3})
+    for (int mode = 0; mode < 4; ++mode)
+      for (int nw : {4, 16})
+        for (int vpl = 1; vpl <= qkn::kMaxSlots; ++vpl)
+          for (int narrow = 0; narrow < 2; ++narrow)
+            for (int nt = 0; nt < 2; ++nt)
+              for (int pipe = 0; pipe < 2; ++pipe)
+                for (int rpw : {1, 2, 4}) {
+                  if (!qkn::compiled(dtype, mode, vpl, nw, narrow, nt, pipe, rpw)) continue;
+                  ++compiled_n;
+                  const qkn::VariantKey k{dtype, mode, vpl, nw, narrow != 0, nt != 0, pipe != 0, rpw};
+                  if (!qkn::g_reached.count(k)) unused.push_back(k);
+                }
+  std::printf("entry points: %ld calls, %ld launches, %zu variants reached, %ld compiled, %zu compiled and "
+              "never reached\n", calls, qkn::g_launches, qkn::g_reached.size(), compiled_n, unused.size());
+  CHECK(unused.empty(), "%zu compiled variants that no call reaches", unused.size());
+  for (const auto& k : unused)
+    std::printf("  unreached: dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d\n", std::get<0>(k),
+                std::get<1>(k), std::get<2>(k), std::get<3>(k), (int)std::get<4>(k), (int)std::get<5>(k),
+                (int)std::get<6>(k), std::get<7>(k));
   std::printf("%d cases, %d failures\n", cases, failures);
   return failures ? 1 : 0;
 }
