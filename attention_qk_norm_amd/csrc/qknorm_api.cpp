@@ -428,13 +428,21 @@ void share_gamma(qkn::Seg* s, int dtype) {
   s->lds_gamma = (s->rows_per_wg > 1 && gamma_bytes(s->row_bytes, dtype) <= kLdsGammaMax) ? 1 : 0;
 }
 
-// Statistics-only launches (partial sums, inverse RMS) over rows of at most
-// 2 slots, one wavefront each, and many of them (16 or more per SIMD): each
-// wavefront takes 4 rows (1 slot) or 2 rows (2 slots) at once, so it keeps 4
-// or 2 times the loads in flight. A read-only pass has no stores to overlap
-// its load latency with: 16384 rows of 1024 bf16 columns 8.16 -> 6.97 us,
-// 32768 of 512: 8.52 -> 7.48 us, 16384 of 2048 fp8: 7.49 -> 7.13 us. Passes
-// that also write were neutral to 4% slower and keep one row per wavefront.
+// Launches over many narrow rows, one wavefront each (16 or more rows per
+// SIMD): each wavefront takes several rows at once, so it keeps several
+// times the loads in flight and its fixed costs (argument loads, offsets,
+// the weights) serve several rows.
+//  - Statistics-only launches (partial sums, inverse RMS) over rows of 1 or
+//    2 slots take 4 or 2 rows: a read-only pass has no stores to overlap its
+//    load latency with (16384 rows of 1024 bf16 columns 8.16 -> 6.97 us,
+//    32768 of 512: 8.52 -> 7.48 us, 16384 of 2048 fp8: 7.49 -> 7.13 us).
+//  - Forward and apply launches over rows of 1 slot take 4 rows (MI355X,
+//    q and k rows of the same shape: bf16 8192 x 512 6.94 us against 7.98
+//    with one row per wavefront, 65536 x 512 44.5 against 45.5, fp32
+//    65536 x 256 44.0 against 45.8, fp8 32768 x 1024 25.3 against 27.3;
+//    apply on 8192 x 512: 7.0 against 8.5). With 2 slots, 2 rows per
+//    wavefront were 0-3% slower (bf16 65536 x 1024: 85.4 against 83.7), so
+//    those keep one row per wavefront.
 //
 // FP8 forward launches that are a single round of one-wavefront rows (fewer
 // than 8 rows per SIMD, at most 8 slots) take 2 rows per wavefront: FP8 rows
@@ -454,7 +462,8 @@ void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nse
   }
   const int64_t simds = int64_t{4} * ctx->num_cus;
   int rpw = 1;
-  if (v->mode == qkn::MODE_STATS && slots <= 2 && a->T * nseg >= 16 * simds)
+  const bool many = a->T * nseg >= 16 * simds;
+  if (v->nt && many && (slots == 1 || (slots == 2 && v->mode == qkn::MODE_STATS)) && v->mode != qkn::MODE_HEAD)
     rpw = slots == 1 ? 4 : 2;
   else if (v->mode == qkn::MODE_FWD && v->dtype == QKNORM_FP8_E4M3 && v->nt && slots <= 8 &&
            a->T * nseg < 8 * simds)

@@ -281,14 +281,32 @@ __device__ __forceinline__ float add_lanes_in_order(float S, float v, int l0, in
   return S;
 }
 
+// Sums over the 64 lanes of a wavefront of R independent values at once
+// (one per row a wavefront holds); every lane receives the same sums. Each
+// step is applied to all R values before the next, so the steps of
+// different rows fill each other's pipeline gaps, while every value is
+// added in the same order as on its own. Must be called with all 64 lanes
+// active.
+template <int R>
+__device__ __forceinline__ void wave_sums(float (&v)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] += dpp<0xB1>(v[r]);   // quad_perm [1,0,3,2]: pairs
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] += dpp<0x4E>(v[r]);   // quad_perm [2,3,0,1]: quads
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] += dpp<0x141>(v[r]);  // row_half_mirror: 8 lanes
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] += dpp<0x140>(v[r]);  // row_mirror: 16 lanes (row sums)
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    v[r] = (lane_value(v[r], 0) + lane_value(v[r], 16)) + (lane_value(v[r], 32) + lane_value(v[r], 48));
+}
+
 // Sum over the 64 lanes of a wavefront; every lane receives the same value.
-// Must be called with all 64 lanes active.
 __device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: pairs
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: quads
-  v += dpp<0x141>(v);  // row_half_mirror: 8 lanes
-  v += dpp<0x140>(v);  // row_mirror: 16 lanes (every lane of a row holds the row sum)
-  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+  float a[1] = {v};
+  wave_sums<1>(a);
+  return a[0];
 }
 
 // Exact v / sv for 0 <= v < 2^20, 1 <= sv < 2^20: a float estimate off by at
@@ -630,17 +648,29 @@ __device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const typenam
       row_rsrc<E>(s.y, s.y_stride, row, live, s.row_bytes), L);
 }
 
+// The split path's precomputed partials of a row (MODE_APPLY): lane k <
+// comb_k fetches partial k, laid out [comb_k][T]. Issued with the row's own
+// loads, so its round trip overlaps theirs; other modes load nothing.
+template <int MODE>
+__device__ __forceinline__ float load_partial(const Hot& s, int64_t row, bool live, int lane) {
+  if constexpr (MODE == MODE_APPLY)
+    return (live && lane < s.comb_k) ? s.stats_in[static_cast<int64_t>(lane) * s.T + row] : 0.f;
+  return 0.f;
+}
+// Loads load_partial adds to a wavefront's count of outstanding loads.
+template <int MODE>
+constexpr int kPartialLoads = MODE == MODE_APPLY ? 1 : 0;
+
 // Finish one row whose data (and weights) are in registers: statistic (or
-// the precomputed partials), then scale and store, or publish the statistic.
+// the precomputed partials `pk`, from load_partial), then scale and store,
+// or publish the statistic.
 template <class E, int VPL, int MODE, bool NARROW, bool NT, bool CHECK = E::kSaturates>
 __device__ __forceinline__ void row_finish(const u32x4 (&d)[VPL], const typename E::G (&g)[VPL], const Hot& s,
                                            const Layout<VPL>& L, int64_t row, bool live, int wave,
-                                           int lane, float* part, bool reuse) {
+                                           int lane, float* part, bool reuse, float pk) {
   float S = 0.f;
   if constexpr (MODE == MODE_APPLY) {
-    // lane k fetches partial k; then they are added in ascending k
-    float pk = 0.f;
-    if (live && lane < s.comb_k) pk = s.stats_in[static_cast<int64_t>(lane) * s.T + row];
+    // lane k holds partial k; they are added in ascending k
     S = add_lanes_in_order(S, pk, 0, 1, s.comb_k);
   } else {
     S = row_stat<E, VPL, NARROW>(d, s, L, wave, lane, part, reuse);
@@ -744,27 +774,81 @@ __device__ __forceinline__ void fwd_pipelined(const Hot& s, const Layout<VPL>& L
   }
 }
 
+// The statistic of each of the RPW rows a one-wavefront team holds
+// (sub-teams of whole wavefronts): per slice, the lane sums of all rows
+// reduce together (wave_sums), then each row adds its slices in ascending
+// order, as row_stat does for one row, so the results are the same bits.
+template <class E, int V, int RPW>
+__device__ __forceinline__ void stat_rows(const u32x4 (&d)[RPW][V], const Hot& s, float (&S)[RPW]) {
+  float p[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    S[r] = 0.f;
+    p[r] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) p[r] = E::sumsq(d[r][j], p[r]);
+    if ((s.flush_mask >> j) & 1u) {
+      wave_sums<RPW>(p);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        S[r] += p[r];
+        p[r] = 0.f;
+      }
+    }
+  }
+}
+
+// Publish the statistics of RPW consecutive rows (statistics-only passes).
+template <int RPW>
+__device__ __forceinline__ void store_stats(const float (&S)[RPW], const Hot& s, int64_t row0, int tl) {
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+    if (row0 + r < s.T && tl == 0) s.stats_out[row0 + r] = s.emit_rinv ? inv_rms(S[r], s.inv_h, s.eps) : S[r];
+}
+
 // One wavefront per row, RPW consecutive rows per wavefront: all their loads
 // go out first, then the rows are finished in order, so the work on one row
 // overlaps the loads of the next; the rows share one copy of the weights.
-// Each row is reduced by the wavefront on its own (no LDS).
+// Each row is reduced by the wavefront on its own (no LDS); statistics-only
+// passes reduce all the rows together.
 template <class E, int V, int NW, int MODE, bool NT, int RPW>
 __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int wave, int lane, float* part,
                                           u32x4* lds_g) {
   int64_t gi = blockIdx.x;
   int64_t row0 = (gi * s.rows_per_wg + L.team) * RPW;
   u32x4 d[RPW][V];
+  float pk[RPW];
   typename E::G g[V];
   const bool staged = MODE != MODE_STATS && s.lds_gamma;
   if (staged) gamma_to_lds<E, V, NW>(s, wave, lane, lds_g);
 #pragma unroll
-  for (int r = 0; r < RPW; ++r)
+  for (int r = 0; r < RPW; ++r) {
     load_row<E, V, NT>(d[r], row_rsrc<E>(s.x, s.x_stride, row0 + r, row0 + r < s.T, s.row_bytes), L);
+    pk[r] = load_partial<MODE>(s, row0 + r, row0 + r < s.T, lane);
+  }
   if constexpr (MODE != MODE_STATS) {
     if (staged)
-      gamma_from_lds<E, V, V * RPW>(g, s, L, lds_g);
+      gamma_from_lds<E, V, (V + kPartialLoads<MODE>) * RPW>(g, s, L, lds_g);
     else
       load_gamma<E, V>(g, s, L);
+  }
+  if constexpr (MODE == MODE_STATS) {
+    float S[RPW];
+    stat_rows<E, V, RPW>(d, s, S);
+    store_stats<RPW>(S, s, row0, L.tl);
+    // grids capped at the hardware limit only
+    for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
+      row0 = (gi * s.rows_per_wg + L.team) * RPW;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        load_row<E, V, NT>(d[r], row_rsrc<E>(s.x, s.x_stride, row0 + r, row0 + r < s.T, s.row_bytes), L);
+      stat_rows<E, V, RPW>(d, s, S);
+      store_stats<RPW>(S, s, row0, L.tl);
+    }
+    return;
   }
   // FP8 forward: when the weights alone bound every result inside the range
   // (checked once for all the wavefront's rows), the rows skip the
@@ -774,22 +858,25 @@ __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int 
   if (check) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
-      row_finish<E, V, MODE, false, NT>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false);
+      row_finish<E, V, MODE, false, NT>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false, pk[r]);
   } else {
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
-      row_finish<E, V, MODE, false, NT, false>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false);
+      row_finish<E, V, MODE, false, NT, false>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false,
+                                               pk[r]);
   }
   // grids capped at the hardware limit only
   for (gi += gridDim.x; gi < s.nwg; gi += gridDim.x) {
     row0 = (gi * s.rows_per_wg + L.team) * RPW;
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
+    for (int r = 0; r < RPW; ++r) {
       load_row<E, V, NT>(d[r], row_rsrc<E>(s.x, s.x_stride, row0 + r, row0 + r < s.T, s.row_bytes), L);
+      pk[r] = load_partial<MODE>(s, row0 + r, row0 + r < s.T, lane);
+    }
     if constexpr (MODE != MODE_STATS) load_gamma<E, V>(g, s, L);
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
-      row_finish<E, V, MODE, false, NT>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false);
+      row_finish<E, V, MODE, false, NT>(d[r], g, s, L, row0 + r, row0 + r < s.T, wave, lane, part, false, pk[r]);
   }
 }
 
@@ -830,14 +917,15 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
     const bool staged = MODE != MODE_STATS && s.lds_gamma;
     if (staged) gamma_to_lds<E, V, NW>(s, wave, lane, lds_g);
     load_row<E, V, NT>(d, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
+    const float pk = load_partial<MODE>(s, row, live, lane);
     if constexpr (MODE != MODE_STATS) {
       if (staged)
-        gamma_from_lds<E, V>(g, s, L, lds_g);
+        gamma_from_lds<E, V, V + kPartialLoads<MODE>>(g, s, L, lds_g);
       else
         load_gamma<E, V>(g, s, L);
     }
     row_finish<E, V, MODE, NARROW, NT>(d, g, s, L, row, live, wave, lane, part,
-                                       gi + static_cast<int64_t>(gridDim.x) < s.nwg);
+                                       gi + static_cast<int64_t>(gridDim.x) < s.nwg, pk);
     // Only grids capped at the hardware limit get here. Reloading gamma each
     // time keeps the first row's registers free of this loop (holding them
     // across it costs about 40 VGPRs).
@@ -847,9 +935,10 @@ __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wa
       u32x4 d2[V];
       typename E::G g2[V];
       load_row<E, V, NT>(d2, row_rsrc<E>(s.x, s.x_stride, row, live, s.row_bytes), L);
+      const float pk2 = load_partial<MODE>(s, row, live, lane);
       if constexpr (MODE != MODE_STATS) load_gamma<E, V>(g2, s, L);
       row_finish<E, V, MODE, NARROW, NT>(d2, g2, s, L, row, live, wave, lane, part,
-                                         gi + static_cast<int64_t>(gridDim.x) < s.nwg);
+                                         gi + static_cast<int64_t>(gridDim.x) < s.nwg, pk2);
     }
   }
 }

@@ -170,9 +170,9 @@ inline int compiled_vpl(int slots, int nw, int dtype) {
 // none reaches).
 //  - slot counts: those of kVpl4 / kVpl16 up to the type's register cap;
 //  - several rows per wavefront (rpw 2 or 4): 4-wavefront workgroups of
-//    whole-wavefront sub-teams, streaming, unpipelined; statistics-only
-//    passes over rows of 1 slot (4 rows) or 2 slots (2 rows), or FP8
-//    forward passes with 2 rows;
+//    whole-wavefront sub-teams, streaming, unpipelined; rows of 1 slot (4
+//    rows, every mode but the headwise one), statistics-only passes over
+//    rows of 2 slots (2 rows), or FP8 forward passes with 2 rows;
 //  - the persistent pipelined body: forward passes in 4-wavefront
 //    workgroups;
 //  - narrow-slice kernels stream (nt) and never serve the headwise form or
@@ -193,7 +193,7 @@ constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool 
   if (!compiled_vpl_value(vpl, nw, dtype)) return false;
   if (rpw != 1) {
     if (nw != 4 || narrow || !nt || pipe) return false;
-    return (mode == MODE_STATS && ((vpl == 1 && rpw == 4) || (vpl == 2 && rpw == 2))) ||
+    return (vpl == 1 && rpw == 4 && mode != MODE_HEAD) || (mode == MODE_STATS && vpl == 2 && rpw == 2) ||
            (mode == MODE_FWD && dtype == QKNORM_FP8_E4M3 && rpw == 2);
   }
   if (narrow && !nt) return false;

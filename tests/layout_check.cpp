@@ -208,8 +208,10 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
       CHECK(int64_t{a.seg[i].nwg} * per_wg >= T && int64_t{a.seg[i].nwg - 1} * per_wg < T, "%s nwg %d", what,
             a.seg[i].nwg);
       CHECK(v.rpw == 1 || (a.seg[i].wpr_log2 == 0 && !narrow && nw == 4 &&
-                           (mode == qkn::MODE_STATS ? a.seg[i].nslot * v.rpw <= 4
-                                                    : dtype == QKNORM_FP8_E4M3 && v.rpw == 2 && a.seg[i].nslot <= 8)),
+                           ((mode == qkn::MODE_STATS && a.seg[i].nslot * v.rpw <= 4) ||
+                            (a.seg[i].nslot == 1 && v.rpw == 4) ||
+                            (mode == qkn::MODE_FWD && dtype == QKNORM_FP8_E4M3 && v.rpw == 2 &&
+                             a.seg[i].nslot <= 8))),
             "%s mode %d rpw %d with wpr_log2 %d, %d slots", what, mode, v.rpw, a.seg[i].wpr_log2, a.seg[i].nslot);
     }
   }

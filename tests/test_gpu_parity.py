@@ -611,11 +611,19 @@ ROWS_PER_WAVE = [
     ("f32", 20001, 256, None, 1),
     ("f32", 17003, 512, 128, 4),
     ("fp8", 17000, 1024, 2048, 1),
+    # rows of 1 slot: forward and apply launches take 4 rows per wavefront too
+    ("bf16", 9001, 512, 512, 1),
+    ("bf16", 12000, 512, None, 1),
+    ("fp8", 17000, 1024, 1024, 1),
 ]
 
 
 @pytest.mark.parametrize("dtype,T,Hq,Hk,K", ROWS_PER_WAVE)
 def test_rows_per_wavefront(dtype, T, Hq, Hk, K):
+    """Parity of every launch that gives a wavefront several rows, and bit
+    equality with the same launches pinned to one row per wavefront (a
+    forced team of one wavefront turns the rule off): a row's arithmetic
+    does not depend on how many rows its wavefront holds."""
     gdt = "bf16" if dtype == "fp8" else dtype
     q = workloads.random_rows(T, Hq, dtype, [T, Hq, 5], dist="laplace")
     k = workloads.random_rows(T, Hk, dtype, [T, Hk, 6]) if Hk else None
@@ -623,12 +631,33 @@ def test_rows_per_wavefront(dtype, T, Hq, Hk, K):
     gk = workloads.random_weights(Hk, gdt, [Hk, 8]) if Hk else None
     say("rows per wavefront", dtype, T, Hq, Hk, K)
     yq, yk = run_forward(q, k, gq, gk, 1e-6, K)
-    assert_parity(yq, oracle.forward(q, gq, 1e-6, K)[0], workloads.DTYPES[dtype], "q")
+    refq, Pq = oracle.forward(q, gq, 1e-6, K)
+    assert_parity(yq, refq, workloads.DTYPES[dtype], "q")
     if Hk:
-        assert_parity(yk, oracle.forward(k, gk, 1e-6, K)[0], workloads.DTYPES[dtype], "k")
+        refk, Pk = oracle.forward(k, gk, 1e-6, K)
+        assert_parity(yk, refk, workloads.DTYPES[dtype], "k")
     rq, _ = qk.inv_rms(gpu(q), eps=1e-6, num_slices=K)
     torch.cuda.synchronize()
     assert_parity(rq, oracle.inv_rms(q, 1e-6, K), torch.float32, "rinv")
+    one = qk.Context(0, waves_per_row=1)
+    yq1, yk1 = run_forward(q, k, gq, gk, 1e-6, K, ctx=one)
+    rq1, _ = qk.inv_rms(gpu(q), eps=1e-6, num_slices=K, ctx=one)
+    torch.cuda.synchronize()
+    assert torch.equal(yq, yq1) and torch.equal(rq, rq1)
+    if Hk:
+        assert torch.equal(yk, yk1)
+    # the split path's apply step over whole rows, given the oracle's partials
+    sq = torch.from_numpy(Pq.astype(np.float32)).to(DEV)
+    sk = torch.from_numpy(Pk.astype(np.float32)).to(DEV) if Hk else None
+    kd, gkd = (gpu(k), gpu(gk)) if Hk else (None, None)
+    aq, ak = qk.apply_stats_qk(gpu(q), kd, gpu(gq), gkd, sq, sk, Hq, Hk or 0, eps=1e-6)
+    aq1, ak1 = qk.apply_stats_qk(gpu(q), kd, gpu(gq), gkd, sq, sk, Hq, Hk or 0, eps=1e-6, ctx=one)
+    torch.cuda.synchronize()
+    assert_parity(aq, refq, workloads.DTYPES[dtype], "apply q")
+    assert torch.equal(aq, aq1)
+    if Hk:
+        assert_parity(ak, refk, workloads.DTYPES[dtype], "apply k")
+        assert torch.equal(ak, ak1)
 
 
 def test_split_path_on_a_rank_slice():
