@@ -10,7 +10,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqkceil.so")
 
 OK, ERR_NULL, ERR_SIZE, ERR_ALIGN, ERR_CONFIG, ERR_DEVICE = 0, -1, -2, -3, -4, -5
-EXPORTS = ("qkceil_copy", "qkceil_read", "qkceil_write", "qkceil_empty")
+EXPORTS = ("qkceil_copy", "qkceil_read", "qkceil_write", "qkceil_empty", "qkceil_clock")
 VECTORS_PER_LANE = (1, 2, 4, 8)
 
 _lib = None
@@ -30,6 +30,7 @@ def lib():
             L.qkceil_read.argtypes = [vp, u64, ci, vp, vp]
             L.qkceil_write.argtypes = [vp, u64, ci, vp]
             L.qkceil_empty.argtypes = [cu, vp]
+            L.qkceil_clock.argtypes = [vp, vp]
             for name in EXPORTS:
                 getattr(L, name).restype = ci
             _lib = L
@@ -55,3 +56,8 @@ def write(dst_ptr, nbytes, vectors_per_lane, stream_ptr):
 
 def empty(workgroups, stream_ptr):
     _check(lib().qkceil_empty(workgroups, stream_ptr), "qkceil_empty")
+
+
+def clock(out_ptr, stream_ptr):
+    """Queue a sample of the shader clock into two uint64 at out_ptr."""
+    _check(lib().qkceil_clock(out_ptr, stream_ptr), "qkceil_clock")

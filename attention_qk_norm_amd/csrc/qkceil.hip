@@ -1,5 +1,6 @@
 // qkceil.hip -- streaming copy, read-only, write-only and empty kernels for
-// gfx950: the bandwidth ceiling the QK-Norm kernels are measured against.
+// gfx950: the bandwidth ceiling the QK-Norm kernels are measured against;
+// and a probe of the shader clock between launches.
 // They move data the way the QK-Norm kernels move rows (raw 16-byte buffer
 // accesses with the non-temporal policy, every load of a lane issued before
 // its stores), with no arithmetic in between.
@@ -69,6 +70,20 @@ __global__ void __launch_bounds__(kLanes) write_kernel(char* __restrict__ dst, u
 }
 
 __global__ void __launch_bounds__(kLanes) empty_kernel() {}
+
+// Cycles of this compute unit's clock over 200 ticks (2 us) of the 100 MHz
+// real-time clock; the loop ends when the real-time clock has advanced.
+__global__ void __launch_bounds__(64) clock_kernel(uint64_t* out) {
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c0 = __builtin_readcyclecounter();
+  uint64_t r1 = r0;
+  while (r1 - r0 < 200) r1 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c1 = __builtin_readcyclecounter();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r1 - r0;
+  }
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -141,6 +156,13 @@ int qkceil_write(void* dst, uint64_t bytes, int vectors_per_lane, void* stream) 
 int qkceil_empty(unsigned workgroups, void* stream) {
   if (workgroups == 0) return QKCEIL_ERR_CONFIG;
   hipLaunchKernelGGL(empty_kernel, dim3(workgroups), dim3(kLanes), 0, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int qkceil_clock(uint64_t* out, void* stream) {
+  if (out == nullptr) return QKCEIL_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0) return QKCEIL_ERR_ALIGN;
+  hipLaunchKernelGGL(clock_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), out);
   return launched();
 }
 

@@ -21,7 +21,10 @@ Beside the headline the line carries, each timed the same way:
     kernels (libqkceil) over the same bytes, and an empty launch;
   - the headwise form, the split path (whole computation, and one rank's
     share on contiguous shards), FP8 rows of the same shape;
-  - the fp64 CPU oracle on the host's cores (median of 5 runs).
+  - the fp64 CPU oracle on the host's cores (median of 5 runs);
+  - the shader clock the back-to-back launches met (a one-wavefront probe
+    between every 10 launches of a separate pass): long runs of the most
+    arithmetic-heavy launches lower it.
 """
 import argparse
 import ctypes
@@ -122,6 +125,29 @@ class Clock:
         e1.record(self.stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n, host_us
+
+    def shader_clock(self, n, fn, every=10):
+        """The shader clock met by n back-to-back steps of fn(i) (gated like
+        region()): a one-wavefront probe (libqkceil) samples it before every
+        `every` steps and after the last; MHz as min / median / max."""
+        from attention_qk_norm_amd import ceiling
+        torch = self.torch
+        m = n // every + 2
+        buf = torch.zeros(2 * m, dtype=torch.int64, device=torch.device("cuda", torch.cuda.current_device()))
+        sp = ctypes.c_void_p(self.stream.cuda_stream)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(self.cyc_per_us * (200.0 + 40.0 * n)))
+        k = 0
+        for i in range(n):
+            if i % every == 0:
+                ceiling.clock(buf.data_ptr() + 16 * k, sp)
+                k += 1
+            fn(i)
+        ceiling.clock(buf.data_ptr() + 16 * k, sp)
+        k += 1
+        torch.cuda.synchronize()
+        mhz = [100.0 * c / r for c, r in buf.cpu().view(-1, 2)[:k].tolist() if r > 0]  # 100 MHz real-time clock
+        return {"min": min(mhz), "median": statistics.median(mhz), "max": max(mhz), "samples": len(mhz)}
 
     def steady(self, n, warmup, fn, launches=1):
         for i in range(warmup):
@@ -250,7 +276,8 @@ def workload_figures(torch, qk, workloads, name, args, ctx, clock, dev, latency=
         step = forward_step(qk, sets, gq, gk, w.eps, K, ctx, clock.stream)
         ms = clock.steady(args.steps, args.warmup, step)
         gbs = ab / (ms * 1e-3) / 1e9
-        fig = {"kernel_us": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3), "gbs": gbs, "frac": gbs / HBM_PEAK_GBS}
+        fig = {"kernel_us": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3), "gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
+               "shader_clock_mhz_back_to_back": clock.shader_clock(args.steps, step)}
         if latency:
             fig["call_to_done_us_p10_p50_p90"] = clock.call_to_done(min(args.steps, 200), step)
         out["K%d" % K] = fig
@@ -366,10 +393,12 @@ def fp8_figures(torch, qk, workloads, name, args, ctx, clock, dev):
         name, w.T, w.hq, w.hk, ", in place" if w.in_place else ""),
         "algorithmic_bytes": w.algorithmic_bytes()}
     for K in w.slices:
-        ms = clock.steady(args.steps, args.warmup, forward_step(qk, sets, gq, gk, w.eps, K, ctx, clock.stream))
+        step = forward_step(qk, sets, gq, gk, w.eps, K, ctx, clock.stream)
+        ms = clock.steady(args.steps, args.warmup, step)
         gbs = w.algorithmic_bytes() / (ms * 1e-3) / 1e9
         out["K%d" % K] = {"kernel_us": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3), "gbs": gbs,
-                          "frac": gbs / HBM_PEAK_GBS}
+                          "frac": gbs / HBM_PEAK_GBS,
+                          "shader_clock_mhz_back_to_back": clock.shader_clock(args.steps, step)}
     del sets
     torch.cuda.empty_cache()
     return out
@@ -504,6 +533,7 @@ def main():
 
     extra = {}
     if not args.main_only:
+        extra["shader_clock_mhz_back_to_back"] = clock.shader_clock(args.steps, step)
         extra.update(secondary(torch, qk, workloads, w, d, args, K, sets, gq, gk, ctx, clock, dev, step))
         del sets
         torch.cuda.empty_cache()

@@ -61,6 +61,15 @@ int qkceil_write(void *dst, uint64_t bytes, int vectors_per_lane, void *stream);
  * the fixed cost of a launch. Status: QKCEIL_ERR_CONFIG, QKCEIL_ERR_DEVICE. */
 int qkceil_empty(unsigned workgroups, void *stream);
 
+/* Samples the shader clock of the compute unit that runs it (one
+ * wavefront): out[0] = cycles of that clock, out[1] = ticks of the fixed
+ * 100 MHz real-time clock, over about 2 us; the clock ran at 100 * out[0] /
+ * out[1] MHz. Queued between other launches, it shows the clock those
+ * launches met. `out` is two 8-byte-aligned uint64 values in device memory.
+ * Status: QKCEIL_ERR_NULL, QKCEIL_ERR_ALIGN (out not 8-byte aligned),
+ * QKCEIL_ERR_DEVICE. */
+int qkceil_clock(uint64_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

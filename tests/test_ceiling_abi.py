@@ -50,3 +50,5 @@ def test_argument_checks(call):
             continue  # the write stream has no source
         assert run(**kw) == want, kw
     assert L.qkceil_empty(0, None) == ceiling.ERR_CONFIG
+    assert L.qkceil_clock(None, None) == ceiling.ERR_NULL
+    assert L.qkceil_clock(A + 4, None) == ceiling.ERR_ALIGN
