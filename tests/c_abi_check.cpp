@@ -1,8 +1,11 @@
 // A C++ caller of libqknorm through include/qknorm.h alone (no Python): device
-// buffers from hipMalloc, the fused forward, the split path and the inverse
-// RMS on fp32 rows, checked element by element against the fp64 oracle
-// (oracle/qknorm_oracle.c, linked as test infrastructure), plus error codes.
-// Prints "c_abi_check: ok" and exits 0 on success.
+// buffers from hipMalloc, then every entry point the header declares on fp32
+// rows (the fused forward with default and forced options, the headwise
+// form, the inverse RMS, the split path one tensor at a time and both
+// tensors at once), checked element by element against the fp64 oracle
+// (oracle/qknorm_oracle.c, linked as test infrastructure), plus error codes,
+// status strings and width limits. Prints "c_abi_check: ok" and exits 0 on
+// success.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -16,6 +19,8 @@ extern "C" void oracle_forward(const float* x, int64_t T, int64_t H, int64_t ldx
                                int K, double* P, double* y, int64_t ldy);
 extern "C" void oracle_inv_rms(const float* x, int64_t T, int64_t H, int64_t ldx, int K, double eps, double* P,
                                double* r);
+extern "C" void oracle_headwise(const float* x, int64_t T, int64_t H, int64_t ldx, int64_t D, const float* gamma,
+                                double eps, double* y, int64_t ldy);
 
 static int failures = 0;
 #define EXPECT(c, ...)                  \
@@ -121,6 +126,91 @@ int main() {
   for (size_t i = 0; i < yq.size(); ++i) bad_q += !close_f32(yq[i], refq[i]);
   EXPECT(bad_q == 0, "%d split-path elements outside 1e-5", bad_q);
 
+  // headwise: heads of 64 columns, weights shared by the heads of a tensor
+  const int64_t D = 64;
+  std::vector<float> hq(D), hk(D);
+  for (int64_t j = 0; j < D; ++j) {
+    hq[j] = 0.75f + (float)(j % 9) / 16.0f;
+    hk[j] = 1.25f - (float)(j % 3) / 4.0f;
+  }
+  float *dhq, *dhk;
+  HIP(hipMalloc(&dhq, D * 4));
+  HIP(hipMalloc(&dhk, D * 4));
+  HIP(hipMemcpy(dhq, hq.data(), D * 4, hipMemcpyHostToDevice));
+  HIP(hipMemcpy(dhk, hk.data(), D * 4, hipMemcpyHostToDevice));
+  HIP(hipMemcpy(dq, q.data(), q.size() * 4, hipMemcpyHostToDevice));  // the split path above wrote in place
+  EXPECT(qknorm_forward_headwise(ctx, QKNORM_F32, T, &rq, &rk, dhq, dhk, D, eps, stream) == QKNORM_OK, "headwise");
+  EXPECT(qknorm_forward_headwise(ctx, QKNORM_F32, T, &rq, &rk, dhq, dhk, 48, eps, stream) == QKNORM_ERR_SLICES,
+         "headwise with a head that is not a power of two of vectors");
+  HIP(hipStreamSynchronize(stream));
+  HIP(hipMemcpy(yq.data(), dyq, yq.size() * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(yk.data(), dyk, yk.size() * 4, hipMemcpyDeviceToHost));
+  std::vector<double> hrefq(q.size()), hrefk(k.size());
+  oracle_headwise(q.data(), T, Hq, Hq, D, hq.data(), (double)eps, hrefq.data(), Hq);
+  oracle_headwise(k.data(), T, Hk, Hk, D, hk.data(), (double)eps, hrefk.data(), Hk);
+  bad_q = bad_k = 0;
+  for (size_t i = 0; i < yq.size(); ++i) bad_q += !close_f32(yq[i], hrefq[i]);
+  for (size_t i = 0; i < yk.size(); ++i) bad_k += !close_f32(yk[i], hrefk[i]);
+  EXPECT(bad_q == 0 && bad_k == 0, "headwise: %d query, %d key elements outside 1e-5", bad_q, bad_k);
+
+  // split path over both tensors at once: K statistics launches, K applies
+  // (out of place), each taking a query slice and a key slice
+  float *dstats_k;
+  HIP(hipMalloc(&dstats_k, K * T * 4));
+  const int64_t wk = Hk / K;
+  for (int s = 0; s < K; ++s) {
+    qknorm_rows sq{dq + s * w, nullptr, w, Hq, 0}, sk{dk + s * wk, nullptr, wk, Hk, 0};
+    EXPECT(qknorm_partial_stats_qk(ctx, QKNORM_F32, T, &sq, &sk, s, K, dstats, dstats_k, stream) == QKNORM_OK,
+           "stats_qk");
+  }
+  for (int s = 0; s < K; ++s) {
+    qknorm_rows aq{dq + s * w, dyq + s * w, w, Hq, Hq}, ak{dk + s * wk, dyk + s * wk, wk, Hk, Hk};
+    EXPECT(qknorm_apply_stats_qk(ctx, QKNORM_F32, T, &aq, &ak, dgq + s * w, dgk + s * wk, dstats, dstats_k, K, Hq,
+                                 Hk, eps, stream) == QKNORM_OK,
+           "apply_qk");
+  }
+  {
+    qknorm_rows sq{dq, nullptr, w, Hq, 0};
+    EXPECT(qknorm_partial_stats_qk(ctx, QKNORM_F32, T, &sq, nullptr, K, K, dstats, nullptr, stream) ==
+               QKNORM_ERR_SLICES,
+           "stats_qk with a slice index past the last slice");
+  }
+  HIP(hipStreamSynchronize(stream));
+  HIP(hipMemcpy(yq.data(), dyq, yq.size() * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(yk.data(), dyk, yk.size() * 4, hipMemcpyDeviceToHost));
+  bad_q = bad_k = 0;
+  for (size_t i = 0; i < yq.size(); ++i) bad_q += !close_f32(yq[i], refq[i]);
+  for (size_t i = 0; i < yk.size(); ++i) bad_k += !close_f32(yk[i], refk[i]);
+  EXPECT(bad_q == 0 && bad_k == 0, "split path, both tensors: %d query, %d key elements outside 1e-5", bad_q, bad_k);
+
+  // a context with forced options: two wavefronts per row, a capped grid
+  qknorm_options opts{2, 7, 0};
+  qknorm_ctx* ctx2 = nullptr;
+  EXPECT(qknorm_create_ex(&ctx2, 0, &opts) == QKNORM_OK, "create_ex");
+  qknorm_options bad_opts{3, 0, 0};
+  qknorm_ctx* ctx3 = nullptr;
+  EXPECT(qknorm_create_ex(&ctx3, 0, &bad_opts) != QKNORM_OK && ctx3 == nullptr, "create_ex with 3 waves per row");
+  EXPECT(qknorm_forward(ctx2, QKNORM_F32, T, &rq, &rk, dgq, dgk, eps, K, stream) == QKNORM_OK, "forward, forced");
+  HIP(hipStreamSynchronize(stream));
+  HIP(hipMemcpy(yq.data(), dyq, yq.size() * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(yk.data(), dyk, yk.size() * 4, hipMemcpyDeviceToHost));
+  bad_q = bad_k = 0;
+  for (size_t i = 0; i < yq.size(); ++i) bad_q += !close_f32(yq[i], refq[i]);
+  for (size_t i = 0; i < yk.size(); ++i) bad_k += !close_f32(yk[i], refk[i]);
+  EXPECT(bad_q == 0 && bad_k == 0, "forced options: %d query, %d key elements outside 1e-5", bad_q, bad_k);
+  EXPECT(qknorm_destroy(ctx2) == QKNORM_OK, "destroy ctx2");
+
+  // status strings and width limits
+  for (int st : {(int)QKNORM_OK, (int)QKNORM_ERR_NULL, (int)QKNORM_ERR_DTYPE, (int)QKNORM_ERR_SLICES,
+                 (int)QKNORM_ERR_CONTEXT, -12345})
+    EXPECT(qknorm_status_string(st) != nullptr && qknorm_status_string(st)[0] != 0, "status string %d", st);
+  EXPECT(qknorm_max_width(QKNORM_F32) == 32768 && qknorm_max_width(QKNORM_BF16) == 65536 &&
+             qknorm_max_width(QKNORM_FP8_E4M3) == 65536 && qknorm_max_width(7) == 0,
+         "max widths");
+
+  HIP(hipFree(dhq));
+  HIP(hipFree(dhk));
+  HIP(hipFree(dstats_k));
   EXPECT(qknorm_destroy(ctx) == QKNORM_OK, "destroy");
   EXPECT(qknorm_destroy(nullptr) == QKNORM_OK, "destroy(NULL)");
   HIP(hipStreamDestroy(stream));

@@ -1,6 +1,8 @@
 """The C ABI from a C++ caller (tests/c_abi_check.cpp): device buffers from
-hipMalloc, the fused forward, the inverse RMS and the split path against the
-fp64 oracle, and the documented error codes, with no Python in between."""
+hipMalloc, every entry point of include/qknorm.h (fused forward with default
+and forced options, headwise, inverse RMS, the split path for one tensor and
+for both at once) against the fp64 oracle, and the documented error codes,
+status strings and width limits, with no Python in between."""
 import os
 import subprocess
 
