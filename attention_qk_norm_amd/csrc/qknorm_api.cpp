@@ -380,6 +380,7 @@ void fill_layout(qkn::Seg* s, const Plan& p, int nw, int64_t nvec, int K, int64_
   s->slice_vec = static_cast<int32_t>(slice_vec);
   s->inv_slice_vec = 1.0f / static_cast<float>(slice_vec);
   s->lds_gamma = 0;
+  s->lds_gamma_vec = 0;
   s->flush_mask = 0;
   // no slot needs a lane test (qkn::slot_offset)
   s->dense = (p.masked || K == 1 || slice_vec % ns == 0) ? 1 : 0;
@@ -476,11 +477,53 @@ void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nse
   }
 }
 
+// Paired rows: a forward launch of two segments whose rows are each one
+// slice in one wavefront (with staged weights) gives each wavefront one
+// token's row of both, when that makes 1.75 to 4 paired wavefronts per SIMD.
+// A workgroup then stores only after both of its rows have arrived, so the
+// launch issues nearly all its reads before its writes, where separate
+// wavefronts let the narrower rows' stores start while most rows are still
+// being read; reads and writes mixed in HBM cost more than either alone (24
+// MiB each way: 4.99 us read only, 4.78 us write only, 9.87 us as one copy).
+// MI355X, gated back to back, bit for bit the unpaired results, against the
+// unpaired launch: C4 (2048 x 5120/1024 bf16) 9.49 -> 8.95 us; 2048 x
+// 4096/1024 8.51 -> 7.59; 1792 x 4096/4096 12.53 -> 11.09; 3072 x 2048/512
+// 6.81 -> 6.30; fp32 2048 x 2048/512 8.99 -> 8.31. Outside the band it loses:
+// with fewer wavefronts than about two per SIMD the pair's longer chain is
+// exposed (1536 x 4096/4096: 9.90 -> 10.60), and from about five per SIMD
+// the other wavefronts already overlap each row's chain (8192 x 5120/1024:
+// 33.7 -> 34.5). FP8 rows keep their own single-round rule (two rows of one
+// tensor per wavefront): pairing them is within +-3% of it at 2048 tokens.
+bool pair_band(int64_t T, int num_cus) {
+  const int64_t simds = int64_t{4} * num_cus;
+  return 4 * T >= 7 * simds && T <= 4 * simds;
+}
+void pair_rows(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
+  v->pair = false;
+  if (nseg != 2 || v->mode != qkn::MODE_FWD || v->dtype == QKNORM_FP8_E4M3 || v->nw != 4 || v->narrow || !v->nt ||
+      v->pipe || ctx->opt.max_workgroups > 0 || ctx->opt.waves_per_row != 0)
+    return;
+  for (int i = 0; i < 2; ++i)
+    if (a->seg[i].wpr_log2 != 0 || a->seg[i].lay_k != 1 || !a->seg[i].lds_gamma) return;
+  if (!pair_band(a->T, ctx->num_cus)) return;
+  if (a->seg[1].nslot > a->seg[0].nslot) {  // segment 0 is the wider
+    const qkn::Seg t = a->seg[0];
+    a->seg[0] = a->seg[1];
+    a->seg[1] = t;
+  }
+  for (int i = 0; i < 2; ++i) a->seg[i].rpw = 1;
+  v->rpw = 1;
+  v->pair = true;
+  v->vpl_b = qkn::body_slots(v->vpl, a->seg[1].nslot);
+}
+
 // Enqueue `nseg` segments: grid.x covers the larger segment (capped by the
-// persistent-grid option), grid.y selects the segment. A capped forward uses
-// the pipelined variant, whose workgroups prefetch their next rows.
+// persistent-grid option), grid.y selects the segment (paired launches: one
+// row of both). A capped forward uses the pipelined variant, whose
+// workgroups prefetch their next rows.
 int run(const qknorm_ctx* ctx, qkn::Variant v, qkn::Args a, int nseg, void* stream) {
-  rows_per_wave(ctx, &v, &a, nseg);
+  pair_rows(ctx, &v, &a, nseg);
+  if (!v.pair) rows_per_wave(ctx, &v, &a, nseg);
   int64_t gx = 0;
   unsigned lds = 0;
   for (int i = 0; i < nseg; ++i) {
@@ -488,7 +531,13 @@ int run(const qknorm_ctx* ctx, qkn::Variant v, qkn::Args a, int nseg, void* stre
     // whole chunks of one 16-byte vector per thread (see the kernel's gamma_to_lds)
     const unsigned chunk = 16u * 64u * static_cast<unsigned>(v.nw);
     const unsigned need = (gamma_bytes(a.seg[i].row_bytes, v.dtype) + chunk - 1) / chunk * chunk;
-    if (a.seg[i].lds_gamma && need > lds) lds = need;
+    if (v.pair) {
+      // segment 1's weights follow segment 0's
+      a.seg[i].lds_gamma_vec = static_cast<int32_t>(lds / 16u);
+      lds += need;
+    } else if (a.seg[i].lds_gamma && need > lds) {
+      lds = need;
+    }
   }
   if (gx <= 0) return QKNORM_OK;
   const int cap = ctx->opt.max_workgroups;
@@ -501,8 +550,8 @@ int run(const qknorm_ctx* ctx, qkn::Variant v, qkn::Args a, int nseg, void* stre
   // grid-stride loop covers any rows beyond that
   const int64_t hw_cap = int64_t{0xFFFFFFFF} / (int64_t{64} * v.nw);
   if (gx > hw_cap) gx = hw_cap;
-  const hipError_t e = qkn::launch(v, a, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(nseg)), lds,
-                                   static_cast<hipStream_t>(stream));
+  const hipError_t e = qkn::launch(v, a, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(v.pair ? 1 : nseg)),
+                                   lds, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QKNORM_OK : QKNORM_ERR_DEVICE;
 }
 

@@ -329,7 +329,7 @@ struct Hot {
   float* stats_out;
   int64_t x_stride, y_stride, T;
   int rows_per_wg, nwg, nslot, wpr_log2, sub_lanes_log2, lds_gamma, lay_k, comb_k, masked, slice_vec,
-      head_log2, emit_rinv, dense, tail_lanes;
+      head_log2, emit_rinv, dense, tail_lanes, lds_gamma_vec;
   uint32_t row_bytes, flush_mask;
   float inv_slice_vec, h, inv_h, eps;
 
@@ -338,9 +338,35 @@ struct Hot {
         x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
         nslot(s.nslot), wpr_log2(s.wpr_log2), sub_lanes_log2(s.sub_lanes_log2), lds_gamma(s.lds_gamma),
         lay_k(s.lay_k), comb_k(s.comb_k), masked(s.masked), slice_vec(s.slice_vec), head_log2(s.head_log2),
-        emit_rinv(s.emit_rinv), dense(s.dense), tail_lanes(s.tail_lanes),
+        emit_rinv(s.emit_rinv), dense(s.dense), tail_lanes(s.tail_lanes), lds_gamma_vec(s.lds_gamma_vec),
         row_bytes(s.row_bytes), flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h),
         inv_h(s.inv_h), eps(a.eps) {}
+
+  // A segment of a paired launch, whose rows are one slice in one
+  // wavefront: everything but the first fields of the segment (pointers,
+  // strides, row bytes, 1/H) is implied, so only those are loaded. The
+  // layout is the plain strided one (slot j, lane l: vector 64 j + l) with
+  // its V slots and one flush at the last; slots past the row read zeros,
+  // whose squares add nothing, and their stores are dropped.
+  template <int V>
+  __device__ __forceinline__ void paired_one_slice() {
+    wpr_log2 = 0;
+    sub_lanes_log2 = 6;
+    rows_per_wg = 4;
+    masked = 0;
+    lds_gamma = 1;
+    lay_k = 1;
+    dense = 1;
+    nslot = V;
+    flush_mask = 1u << (V - 1);
+    tail_lanes = kWave;
+    slice_vec = 0;
+    // the few arguments left, pinned here so that their loads issue together
+    // at entry (left alone, the compiler sinks some of them past the weight
+    // copies, a second and third round trip before the first row load)
+    asm volatile("" : "+s"(x), "+s"(y), "+s"(gamma), "+s"(x_stride), "+s"(y_stride), "+s"(row_bytes), "+s"(inv_h),
+                 "+s"(T), "+s"(eps));
+  }
 };
 
 // The segment's slot table (each slot's first vector), read at kernel entry
@@ -370,6 +396,16 @@ struct Layout {
   int wpr_log2, wpr, team, tl;
   uint32_t off[V];  // byte offset of each slot's vector; kOutside, or past the row, when empty
   int base[V];      // vector index of each slot, also when empty (masked layout)
+
+  // One slice, a one-wavefront team: slot j of lane l holds vector 64 j + l
+  // (offsets past the row are dropped by the range check).
+  __device__ __forceinline__ Layout(int wave, int lane) : wpr_log2(0), wpr(1), team(wave), tl(lane) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      base[j] = j * kWave + lane;
+      off[j] = static_cast<uint32_t>(base[j]) * 16u;
+    }
+  }
 
   template <int VPL>
   __device__ __forceinline__ Layout(const Tables<VPL>& tb, const Hot& s, int wave, int lane) {
@@ -729,16 +765,27 @@ __device__ __forceinline__ void gamma_to_lds(const Hot& s, int wave, int lane, u
 // at most that many loads may stay in flight), then for the whole
 // workgroup's. Empty slots (offsets at or past the row's end) read the last
 // weight vector: their rows are zeros and their stores are dropped.
-template <class E, int VPL, int INFLIGHT = VPL>
-__device__ __forceinline__ void gamma_from_lds(typename E::G (&g)[VPL], const Hot& s, const Layout<VPL>& L,
+template <class E, int VPL>
+__device__ __forceinline__ void gamma_read_lds(typename E::G (&g)[VPL], const Hot& s, const Layout<VPL>& L,
                                                const u32x4* lds_g) {
   const uint32_t last = (s.row_bytes >> 4) - 1u;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) g[j] = E::gamma_lds(lds_g, min(L.off[j] >> 4, last));
+}
+
+template <int INFLIGHT>
+__device__ __forceinline__ void wait_gamma_copies() {
   static_assert(INFLIGHT < 64, "vmcnt holds 6 bits");
   // s_waitcnt with vmcnt = INFLIGHT and the lgkm / exp counters left alone
   __builtin_amdgcn_s_waitcnt((INFLIGHT & 0xF) | ((INFLIGHT >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) g[j] = E::gamma_lds(lds_g, min(L.off[j] >> 4, last));
+}
+
+template <class E, int VPL, int INFLIGHT = VPL>
+__device__ __forceinline__ void gamma_from_lds(typename E::G (&g)[VPL], const Hot& s, const Layout<VPL>& L,
+                                               const u32x4* lds_g) {
+  wait_gamma_copies<INFLIGHT>();
+  gamma_read_lds<E, VPL>(g, s, L, lds_g);
 }
 
 // Persistent workgroups: group gi, gi + G, gi + 2G, ... (G = gridDim.x). The
@@ -960,37 +1007,99 @@ __device__ __forceinline__ void dispatch(const Hot& s, const Tables<VPL>& tb, in
   body<E, V, VPL, NW, MODE, NARROW, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
 }
 
+// Paired rows: each one-wavefront team takes token t's row of segment a (the
+// wider, VA slots) and of segment b (VB slots), one slice each, and the
+// workgroup stages both weight vectors in LDS (b's after a's). Every row load
+// goes out before the first wait, and each row is finished exactly as on its
+// own (the same strided layout, the same order of operations, so the same
+// bits). Launches of one or a few rounds of wavefronts then issue all their
+// reads before nearly any write: a workgroup stores only after both of its
+// rows have arrived, where separate wavefronts for the two segments let the
+// narrow rows' stores start while most rows are still being read.
+template <class E, int VA, int VB, int NW, bool NT>
+__device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave, int lane, float* part,
+                                          u32x4* lds_g) {
+  const Layout<VA> La(wave, lane);
+  const Layout<VB> Lb(wave, lane);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const bool live = row < sa.T;
+  u32x4 da[VA], db[VB];
+  typename E::G ga[VA], gb[VB];
+  // segment b's weights follow segment a's copy, rounded up to whole chunks
+  // of one vector per thread as the copy loop writes them
+  constexpr uint32_t kChunkVec = NW * kWave;
+  const uint32_t a_vec = (sa.row_bytes * E::kGammaScale) >> 4;
+  u32x4* const lds_b = lds_g + (a_vec + kChunkVec - 1) / kChunkVec * kChunkVec;
+  gamma_to_lds<E, VA, NW>(sa, wave, lane, lds_g);
+  gamma_to_lds<E, VB, NW>(sb, wave, lane, lds_b);
+  load_row<E, VA, NT>(da, row_rsrc<E>(sa.x, sa.x_stride, row, live, sa.row_bytes), La);
+  load_row<E, VB, NT>(db, row_rsrc<E>(sb.x, sb.x_stride, row, live, sb.row_bytes), Lb);
+  wait_gamma_copies<VA + VB>();
+  gamma_read_lds<E, VA>(ga, sa, La, lds_g);
+  gamma_read_lds<E, VB>(gb, sb, Lb, lds_b);
+  // both statistics before any store: the wavefront writes only after all
+  // its reads have landed (the scheduling barrier keeps the compiler from
+  // moving the narrow row's stores up between them)
+  const float Sb = row_stat<E, VB, false>(db, sb, Lb, wave, lane, part, false);
+  const float Sa = row_stat<E, VA, false>(da, sa, La, wave, lane, part, false);
+  __builtin_amdgcn_sched_barrier(0);
+  scale_store<E, VB, NT>(db, gb, Sb, sb, row, live, Lb);
+  scale_store<E, VA, NT>(da, ga, Sa, sa, row, live, La);
+}
+
 // blockIdx.y selects the segment (query rows, key rows), so everything a
-// wavefront needs from the kernel arguments is one round of scalar loads.
-template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW = 1>
+// wavefront needs from the kernel arguments is one round of scalar loads;
+// a paired launch reads both segments in that round.
+template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW = 1, int PAIRB = 0>
 __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   __shared__ float part[NW * kWave];  // per-wavefront slice partials (teams of > 1 wave)
   extern __shared__ u32x4 lds_g[];    // staged gamma (dynamic size: the launch's widest row)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-  const Seg& seg = a.seg[blockIdx.y];
-  const Hot s(a, seg);
-  const Tables<VPL> tb(seg);
-  dispatch<E, VPL, VPL, NW, MODE, NARROW, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
+  if constexpr (PAIRB > 0) {
+    // paired rows: segment 1 runs the body of PAIRB slots (each pairing its
+    // own kernel, so a narrow second row does not carry a wide one's registers)
+    static_assert(MODE == MODE_FWD && NW == 4 && !NARROW && NT && !PIPE && RPW == 1, "paired forward rows only");
+    Hot sa(a, a.seg[0]), sb(a, a.seg[1]);
+    sa.paired_one_slice<VPL>();
+    sb.paired_one_slice<PAIRB>();
+    body_pair<E, VPL, PAIRB, NW, NT>(sa, sb, wave, lane, part, lds_g);
+  } else {
+    const Seg& seg = a.seg[blockIdx.y];
+    const Hot s(a, seg);
+    const Tables<VPL> tb(seg);
+    dispatch<E, VPL, VPL, NW, MODE, NARROW, NT, PIPE, RPW>(s, tb, wave, lane, part, lds_g);
+  }
 }
 
 // The launch dispatch: the run-time variant picks one of the kernels the
 // compiled() table names; any other combination instantiates nothing and is
 // refused.
-template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW>
+template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW, int PAIRB = 0>
 hipError_t launch_one(const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
-  if constexpr (compiled(E::kDtype, MODE, VPL, NW, NARROW, NT, PIPE, RPW)) {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE, NARROW, NT, PIPE, RPW>), gd, dim3(NW * kWave), lds, st, a);
+  if constexpr (compiled(E::kDtype, MODE, VPL, NW, NARROW, NT, PIPE, RPW, PAIRB)) {
+    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE, NARROW, NT, PIPE, RPW, PAIRB>), gd, dim3(NW * kWave), lds, st,
+                       a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
   }
 }
 
+// Paired launches: segment 1's body, down the chain VPL, VPL/2, ...
+template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int VB>
+hipError_t by_pair_b(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
+  if (v.vpl_b == VB) return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 1, VB>(a, gd, lds, st);
+  if constexpr (VB > 1) return by_pair_b<E, VPL, NW, MODE, NARROW, NT, PIPE, VB / 2>(v, a, gd, lds, st);
+  return hipErrorInvalidValue;
+}
+
 template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE>
 hipError_t by_rpw(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
   switch (v.rpw) {
-    case 1: return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 1>(a, gd, lds, st);
+    case 1:
+      return v.pair ? by_pair_b<E, VPL, NW, MODE, NARROW, NT, PIPE, VPL>(v, a, gd, lds, st)
+                    : launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 1>(a, gd, lds, st);
     case 2: return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 2>(a, gd, lds, st);
     case 4: return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 4>(a, gd, lds, st);
     default: return hipErrorInvalidValue;

@@ -28,6 +28,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "qknorm.h"
@@ -49,20 +50,23 @@ constexpr int kMaxSlots = 16;  // slots per lane of the widest compiled variant
 // u * slice_vec to the base and owns slices u, u + nsub, u + 2 nsub, ...
 // (nsub = team lanes / sub-team lanes).
 struct Seg {
+  // first, together (a paired launch reads nothing else of a segment):
   const void* x;          // row 0 of the input
   void* y;                // row 0 of the output (FWD, APPLY, HEAD)
   const void* gamma;      // weights of the columns processed (FWD, APPLY); HEAD: of one head
-  const float* stats_in;  // APPLY: partials laid out [comb_k][T]
-  float* stats_out;       // STATS: row t's sum goes to stats_out[t]
   int64_t x_stride;       // elements between input rows
   int64_t y_stride;       // elements between output rows
+  uint32_t row_bytes;     // bytes of one row processed (and of its weights)
+  float inv_h;            // 1 / h, rounded once (exact for HEAD's power-of-two heads)
+  // the rest of the segment
+  const float* stats_in;  // APPLY: partials laid out [comb_k][T]
+  float* stats_out;       // STATS: row t's sum goes to stats_out[t]
   int32_t wpr_log2;       // log2 of the wavefronts per team
   int32_t sub_lanes_log2; // log2 of the lanes per sub-team (deals one slice at a time)
   int32_t lds_gamma;      // 1: the workgroup stages gamma in LDS and its rows share it
   int32_t rows_per_wg;    // teams per workgroup
   int32_t nwg;            // workgroups covering all T rows
   int32_t nslot;          // slots per lane in use
-  uint32_t row_bytes;     // bytes of one row processed (and of its weights)
   int32_t lay_k;          // partial sums per row (slices)
   int32_t comb_k;         // APPLY: partials combined per row
   int32_t masked;         // masked layout (kernels for narrow slices only)
@@ -71,20 +75,31 @@ struct Seg {
   float h;                // the mean of squares divides by this width
   uint32_t flush_mask;    // segmented layout: bit j set when slot j ends a slice
   int32_t head_log2;      // HEAD: log2 of the 16-byte vectors per head (0 ... 6)
-  float inv_h;            // 1 / h, rounded once (exact for HEAD's power-of-two heads)
   int32_t emit_rinv;      // STATS: write 1 / sqrt(S / h + eps) instead of S
   int32_t rpw;            // rows each one-wavefront team takes at once (1, 2, 4)
   int32_t dense;          // 1: no slot needs a lane test (see slot_offset)
   int32_t tail_lanes;     // lanes of the last slot of each slice (the ragged slot when not dense)
+  int32_t lds_gamma_vec;  // paired launches: where this segment's staged gamma starts in LDS
+                          // (16-byte vectors; 0 for segment 0)
   int32_t slot_base[kMaxSlots];
   int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
+  int32_t pad_[13];             // whole 64-byte lines per segment
 };
 
+// T and eps lead, so that they share a 64-byte line with the first fields of
+// segment 0, and segment 1's first fields sit in one line of their own: a
+// paired launch reads two lines of arguments (arguments are read through
+// scalar loads at kernel entry, and every further line costs time; 512
+// bytes spread over a launch's entry cost about 1.3 us).
 struct Args {
-  Seg seg[2];  // blockIdx.y selects one
   int64_t T;   // rows per segment
   float eps;
+  int32_t pad_;
+  Seg seg[2];  // blockIdx.y selects one (paired launches: both, grid.y = 1)
 };
+static_assert(sizeof(Seg) % 64 == 0, "segments in whole lines");
+static_assert(offsetof(Seg, inv_h) + sizeof(float) <= 48, "a segment's first fields fit the rest of a line");
+static_assert(offsetof(Args, seg) == 16, "segment 0 right after T and eps");
 
 // The row vector that slot j of team lane `tl` holds, or -1 when the slot is
 // empty there. `lim_word` and `base` are the slot's table entries. Used by
@@ -131,7 +146,23 @@ struct Variant {
   bool nt;       // FWD only: non-temporal row loads and stores
   bool pipe;     // FWD only: persistent workgroups with the next rows prefetched
   int rpw = 1;   // rows per one-wavefront team (1, or 2 / 4 for rows of at most 2 slots)
+  bool pair = false;  // FWD: each wavefront takes one token's row of both segments
+                      // (segment 0 the wider), grid.y = 1
+  int vpl_b = 0;      // paired: the body for segment 1's rows, on the chain vpl, vpl/2, ...
 };
+
+// The body for `nslot` slots in a kernel built for `vpl`: the smallest of
+// vpl, vpl/2, vpl/4, ... that holds them (the kernels' dispatch).
+constexpr int body_slots(int vpl, int nslot) {
+  int v = vpl;
+  while (v > 1 && nslot <= v / 2) v /= 2;
+  return v;
+}
+constexpr bool on_halving_chain(int vpl, int v) {
+  for (int c = vpl; c >= 1; c /= 2)
+    if (c == v) return true;
+  return false;
+}
 
 // Slot counts the kernels are compiled for, per workgroup size. In
 // 4-wavefront workgroups every count up to 8 has its own body: a row runs
@@ -177,7 +208,10 @@ inline int compiled_vpl(int slots, int nw, int dtype) {
 //    workgroups;
 //  - narrow-slice kernels stream (nt) and never serve the headwise form or
 //    the split path's apply step, whose layouts hold one slice;
-//  - ordinary cached row accesses (nt off): forward passes only.
+//  - ordinary cached row accesses (nt off): forward passes only;
+//  - paired rows (both segments' rows of a token in one wavefront): fp32 and
+//    bf16 forward passes in 4-wavefront workgroups, streaming, one row of each
+//    segment per wavefront, the second on the chain vpl, vpl/2, ...
 constexpr bool compiled_vpl_value(int vpl, int nw, int dtype) {
   if (vpl < 1 || vpl > max_slots(dtype, nw)) return false;
   if (nw == 4) {
@@ -189,8 +223,12 @@ constexpr bool compiled_vpl_value(int vpl, int nw, int dtype) {
   }
   return false;
 }
-constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool nt, bool pipe, int rpw) {
+constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool nt, bool pipe, int rpw,
+                        int pair_b = 0) {
   if (!compiled_vpl_value(vpl, nw, dtype)) return false;
+  if (pair_b != 0)
+    return mode == MODE_FWD && dtype != QKNORM_FP8_E4M3 && nw == 4 && !narrow && nt && !pipe && rpw == 1 &&
+           on_halving_chain(vpl, pair_b);
   if (rpw != 1) {
     if (nw != 4 || narrow || !nt || pipe) return false;
     return (vpl == 1 && rpw == 4 && mode != MODE_HEAD) || (mode == MODE_STATS && vpl == 2 && rpw == 2) ||
@@ -203,7 +241,7 @@ constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool 
   return true;
 }
 inline bool compiled(const Variant& v) {
-  return compiled(v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw);
+  return compiled(v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0);
 }
 
 // Enqueue one launch: grid.x workgroups per segment, grid.y segments, with

@@ -43,10 +43,12 @@ static Variant g_v;
 static Args g_a;
 static dim3 g_grid;
 static unsigned g_lds;
-using VariantKey = std::tuple<int, int, int, int, bool, bool, bool, int>;
+using VariantKey = std::tuple<int, int, int, int, bool, bool, bool, int, int>;
 static VariantKey key(const Variant& v) {
-  return VariantKey{v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw};
+  return VariantKey{v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0};
 }
+static long g_paired;
+static void check_pair_launch(const Variant& v, const Args& a, dim3 grid, unsigned lds);
 static std::set<VariantKey> g_reached;
 static long g_launches, g_uncompiled;
 hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t) {
@@ -56,6 +58,7 @@ hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes
   g_lds = lds_bytes;
   g_reached.insert(key(v));
   ++g_launches;
+  if (v.pair) check_pair_launch(v, a, grid, lds_bytes);
   if (!compiled(v)) {
     if (g_uncompiled < 10)
       std::printf("FAIL no kernel for reached variant dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d\n",
@@ -86,6 +89,50 @@ static int body_slots(int vpl, int nslot) {  // the kernel's dispatch: VPL, VPL/
   int v = vpl;
   while (v > 1 && nslot <= v / 2) v /= 2;
   return v;
+}
+
+// A paired forward launch (both segments' rows of a token in one
+// wavefront): one-wavefront teams in both segments with staged weights,
+// segment 0 the wider, segment 1 on the body the kernel is built with, the
+// same workgroups covering both, one grid row, and segment 1's weights
+// placed right after segment 0's in LDS.
+void qkn::check_pair_launch(const Variant& v, const Args& a, dim3 grid, unsigned lds) {
+  ++g_paired;
+  const Seg &s0 = a.seg[0], &s1 = a.seg[1];
+  CHECK(v.mode == MODE_FWD && v.nw == 4 && !v.narrow && v.nt && !v.pipe && v.rpw == 1, "paired variant");
+  CHECK(s0.wpr_log2 == 0 && s1.wpr_log2 == 0 && s0.rows_per_wg == 4 && s1.rows_per_wg == 4,
+        "paired teams %d/%d", s0.wpr_log2, s1.wpr_log2);
+  CHECK(s0.lds_gamma && s1.lds_gamma && !s0.masked && !s1.masked && s0.lay_k == 1 && s1.lay_k == 1,
+        "paired segments' weights or layout");
+  // the kernel lays both rows out as plain strided slots (slot j, lane l:
+  // vector 64 j + l, or dropped past the row): the table's layout
+  for (int i = 0; i < 2; ++i) {
+    const Seg& s = a.seg[i];
+    const int nvec = static_cast<int>(s.row_bytes / 16);
+    for (int j = 0; j < s.nslot; ++j)
+      for (int l = 0; l < 64; ++l) {
+        const int v = slot_vector(s.slot_lim[j], s.slot_base[j], l, 0, 6, s.slice_vec, 1);
+        const int want = j * 64 + l < nvec ? j * 64 + l : -1;
+        CHECK(v == want, "paired segment %d slot %d lane %d: table %d, strided %d", i, j, l, v, want);
+      }
+  }
+  CHECK(s0.nslot >= s1.nslot && s0.nslot <= v.vpl && v.vpl_b == body_slots(v.vpl, s1.nslot),
+        "paired slots %d/%d on bodies %d/%d", s0.nslot, s1.nslot, v.vpl, v.vpl_b);
+  CHECK(s0.nwg == s1.nwg && int64_t{s0.nwg} * 4 >= a.T && int64_t{s0.nwg - 1} * 4 < a.T && grid.x == unsigned(s0.nwg) &&
+            grid.y == 1,
+        "paired grid %u x %u for %d workgroups", grid.x, grid.y, s0.nwg);
+  const unsigned chunk = 16u * 64u * 4u;
+  const unsigned need0 = (gamma_bytes(s0.row_bytes, v.dtype) + chunk - 1) / chunk * chunk;
+  const unsigned need1 = (gamma_bytes(s1.row_bytes, v.dtype) + chunk - 1) / chunk * chunk;
+  CHECK(s0.lds_gamma_vec == 0 && unsigned(s1.lds_gamma_vec) * 16u == need0 && lds == need0 + need1,
+        "paired LDS: segment 1 at %d vectors, %u bytes", s1.lds_gamma_vec, lds);
+  // the copy loops of the two bodies cover each segment's weights
+  for (int i = 0; i < 2; ++i) {
+    const int body = i == 0 ? v.vpl : v.vpl_b;
+    const int64_t gvec = gamma_bytes(a.seg[i].row_bytes, v.dtype) / 16;
+    CHECK(gvec <= int64_t{(body + 1) / 2} * 4 * 64 * (v.dtype == QKNORM_FP8_E4M3 ? 2 : 1),
+          "paired segment %d: %lld weight vectors past the copy loop of body %d", i, (long long)gvec, body);
+  }
 }
 
 static void check_seg(const qkn::Seg& s, int nw, int vpl, int64_t nvec, int K, bool masked, const char* what) {
@@ -195,13 +242,18 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
   // up to 8 slots in 4-wavefront workgroups, the widest segment runs a body
   // of exactly its slot count (no empty slots)
   CHECK(nw != 4 || slots > 8 || vpl == slots, "%s %d slots run by the %d-slot body", what, slots, vpl);
-  // several rows per wavefront: every row covered once, no spare workgroups
+  // several rows per wavefront: every row covered once, no spare workgroups;
+  // paired rows (forward only) as the enqueue step decides them
   for (int mode : {qkn::MODE_STATS, qkn::MODE_FWD}) {
     qkn::Variant v{dtype, mode, vpl, nw, narrow, true, false};
     qkn::Args a{};
     a.T = T;
     for (int i = 0; i < nseg; ++i) a.seg[i] = seg[i];
-    rows_per_wave(&ctx, &v, &a, nseg);
+    pair_rows(&ctx, &v, &a, nseg);
+    CHECK(!v.pair || mode == qkn::MODE_FWD, "%s paired rows in mode %d", what, mode);
+    CHECK(!v.pair || (forced_wpr == 0 && pair_band(T, 256) && dtype != QKNORM_FP8_E4M3 && qkn::compiled(v)),
+          "%s paired launch T=%lld", what, (long long)T);
+    if (!v.pair) rows_per_wave(&ctx, &v, &a, nseg);
     for (int i = 0; i < nseg; ++i) {
       const int64_t per_wg = int64_t{a.seg[i].rows_per_wg} * a.seg[i].rpw;
       CHECK(a.seg[i].rpw == v.rpw && (v.rpw == 1 || v.rpw == 2 || v.rpw == 4), "%s rpw %d", what, v.rpw);
@@ -299,8 +351,10 @@ static void print_plan(const char* name, int dtype, int64_t T, int64_t hq, int64
     slots = a.seg[i].nslot > slots ? a.seg[i].nslot : slots;
   }
   qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw, dtype), nw, narrow, true, false};
-  rows_per_wave(&ctx, &v, &a, 2);
-  std::printf("plan %s: nw=%d body=%d narrow=%d rows_per_wave=%d", name, nw, v.vpl, narrow ? 1 : 0, v.rpw);
+  pair_rows(&ctx, &v, &a, 2);
+  if (!v.pair) rows_per_wave(&ctx, &v, &a, 2);
+  std::printf("plan %s: nw=%d body=%d narrow=%d rows_per_wave=%d paired=%d", name, nw, v.vpl, narrow ? 1 : 0, v.rpw,
+              v.pair ? v.vpl_b : 0);
   for (int i = 0; i < 2; ++i)
     std::printf(" | %s team=%d sub_lanes=%d slots=%d masked=%d", i ? "k" : "q", 1 << plans[i].wpr_log2,
                 1 << plans[i].sub_lanes_log2, plans[i].slots, plans[i].masked ? 1 : 0);
@@ -329,7 +383,9 @@ static long sweep_entry_points() {
     qknorm_ctx ctx{0, 256, o};
     for (int dtype : {QKNORM_BF16, QKNORM_F32, QKNORM_FP8_E4M3})
       for (int64_t hq : widths)
-        for (int64_t hk : {hq, hq / 4}) {
+        // key rows as wide as the query rows, or narrower by the grouped-query
+        // ratios (the paired kernels pair a wide row with each narrower body)
+        for (int64_t hk : {hq, hq / 2, hq / 4, hq / 5, hq / 8, hq / 12, hq / 16}) {
           const int64_t ve = vec_elems(dtype);
           if (hq > qknorm_max_width(dtype) || hk < ve || hk % ve) continue;
           for (int64_t T : rows) {
@@ -421,19 +477,20 @@ int main() {
           for (int narrow = 0; narrow < 2; ++narrow)
             for (int nt = 0; nt < 2; ++nt)
               for (int pipe = 0; pipe < 2; ++pipe)
-                for (int rpw : {1, 2, 4}) {
-                  if (!qkn::compiled(dtype, mode, vpl, nw, narrow, nt, pipe, rpw)) continue;
-                  ++compiled_n;
-                  const qkn::VariantKey k{dtype, mode, vpl, nw, narrow != 0, nt != 0, pipe != 0, rpw};
-                  if (!qkn::g_reached.count(k)) unused.push_back(k);
-                }
+                for (int rpw : {1, 2, 4})
+                  for (int pb = 0; pb <= qkn::kMaxSlots; ++pb) {
+                    if (!qkn::compiled(dtype, mode, vpl, nw, narrow, nt, pipe, rpw, pb)) continue;
+                    ++compiled_n;
+                    const qkn::VariantKey k{dtype, mode, vpl, nw, narrow != 0, nt != 0, pipe != 0, rpw, pb};
+                    if (!qkn::g_reached.count(k)) unused.push_back(k);
+                  }
   std::printf("entry points: %ld calls, %ld launches, %zu variants reached, %ld compiled, %zu compiled and "
               "never reached\n", calls, qkn::g_launches, qkn::g_reached.size(), compiled_n, unused.size());
   CHECK(unused.empty(), "%zu compiled variants that no call reaches", unused.size());
   for (const auto& k : unused)
-    std::printf("  unreached: dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d\n", std::get<0>(k),
-                std::get<1>(k), std::get<2>(k), std::get<3>(k), (int)std::get<4>(k), (int)std::get<5>(k),
-                (int)std::get<6>(k), std::get<7>(k));
+    std::printf("  unreached: dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d paired=%d\n",
+                std::get<0>(k), std::get<1>(k), std::get<2>(k), std::get<3>(k), (int)std::get<4>(k),
+                (int)std::get<5>(k), (int)std::get<6>(k), std::get<7>(k), std::get<8>(k));
   std::printf("%d cases, %d failures\n", cases, failures);
   return failures ? 1 : 0;
 }

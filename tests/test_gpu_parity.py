@@ -660,6 +660,58 @@ def test_rows_per_wavefront(dtype, T, Hq, Hk, K):
         assert torch.equal(ak, ak1)
 
 
+PAIRED = [
+    # dtype, T, Hq, Hk, layout: forward launches whose rows of both tensors
+    # are one slice in one wavefront, with 1.75 to 4 paired wavefronts per
+    # SIMD, so each wavefront takes one token's query row and key row
+    ("bf16", 2048, 5120, 1024, "plain"),    # C4's shape
+    ("bf16", 1795, 4096, 1024, "plain"),    # T not a multiple of the 4 rows of a workgroup
+    ("bf16", 3001, 1024, 4096, "plain"),    # key rows wider: the segments swap
+    ("bf16", 4096, 4608, 512, "plain"),     # 9-slot rows on the 10-slot body
+    ("bf16", 2500, 1000, 200, "plain"),     # ragged last slots
+    ("bf16", 2048, 3072, 1024, "in_place"),
+    ("bf16", 2048, 2048, 512, "packed"),    # column blocks of one [T, Hq + Hk + Hv] buffer, in place
+    ("f32", 2048, 2048, 512, "plain"),
+    ("f32", 4000, 1000, 1000, "in_place"),
+]
+
+
+@pytest.mark.parametrize("dtype,T,Hq,Hk,layout", PAIRED)
+def test_paired_rows(dtype, T, Hq, Hk, layout):
+    """Parity of paired launches, and bit equality with the same launch
+    unpaired (a forced team of one wavefront turns pairing off and keeps the
+    rows' layouts): a row's arithmetic does not depend on which row shares
+    its wavefront."""
+    q = workloads.random_rows(T, Hq, dtype, [T, Hq, 11], dist="laplace")
+    k = workloads.random_rows(T, Hk, dtype, [T, Hk, 12])
+    gq = workloads.random_weights(Hq, dtype, [Hq, 13])
+    gk = workloads.random_weights(Hk, dtype, [Hk, 14])
+    say("paired rows", dtype, T, Hq, Hk, layout)
+    refq, _ = oracle.forward(q, gq, 1e-6, 1)
+    refk, _ = oracle.forward(k, gk, 1e-6, 1)
+    outs = []
+    for ctx in (None, qk.Context(0, waves_per_row=1)):
+        if layout == "packed":
+            hv = 256
+            buf = torch.zeros((T, Hq + Hk + hv), dtype=q.dtype)
+            buf[:, :Hq] = q
+            buf[:, Hq:Hq + Hk] = k
+            buf[:, Hq + Hk:] = 7.0
+            bd = gpu(buf)
+            qv, kv = bd[:, :Hq], bd[:, Hq:Hq + Hk]
+            qk.forward(qv, kv, gpu(gq), gpu(gk), eps=1e-6, out_q=qv, out_k=kv, ctx=ctx)
+            torch.cuda.synchronize()
+            assert torch.equal(bd[:, Hq + Hk:].cpu(), buf[:, Hq + Hk:])  # the value columns are untouched
+            yq, yk = qv, kv
+        else:
+            yq, yk = run_forward(q, k, gq, gk, 1e-6, 1, in_place=layout == "in_place", ctx=ctx)
+        outs.append((yq, yk))
+    (yq, yk), (yq1, yk1) = outs
+    assert_parity(yq, refq, workloads.DTYPES[dtype], "q")
+    assert_parity(yk, refk, workloads.DTYPES[dtype], "k")
+    assert torch.equal(yq, yq1) and torch.equal(yk, yk1)
+
+
 def test_split_path_on_a_rank_slice():
     """One rank's share of C5 under 8-way column slicing: slices of 512
     columns of 4096-wide rows, 16384 tokens (each wavefront takes 4 rows)."""
