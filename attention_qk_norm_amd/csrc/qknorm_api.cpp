@@ -445,13 +445,10 @@ void share_gamma(qkn::Seg* s, int dtype) {
 //    wavefront were 0-3% slower (bf16 65536 x 1024: 85.4 against 83.7), so
 //    those keep one row per wavefront.
 //
-// FP8 forward launches that are a single round of one-wavefront rows (fewer
-// than 8 rows per SIMD, at most 8 slots) take 2 rows per wavefront: FP8 rows
-// cost much VALU work (conversions), and with one round there are no other
-// wavefronts to overlap it with memory; a wavefront finishing its first row
-// while its second loads does. C4-fp8 (2048 rows of 5120 + 1024): 8.0 ->
-// 7.15 us. With several rounds the other wavefronts already overlap it
-// (C5-fp8: 46.1 us, against 46.9 with 2 rows).
+// (FP8 forward launches of a single round once took 2 rows of one tensor per
+// wavefront: C4-fp8 8.0 -> 7.15 us at the time. Paired rows serve those
+// launches better, 6.45 -> 6.34 us, and below 2 paired wavefronts per SIMD one
+// row per wavefront is best: 1024 x 5120/1024 4.46 us against 5.57 with two.)
 void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
   for (int i = 0; i < nseg; ++i) a->seg[i].rpw = 1;
   v->rpw = 1;
@@ -466,9 +463,6 @@ void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nse
   const bool many = a->T * nseg >= 16 * simds;
   if (v->nt && many && (slots == 1 || (slots == 2 && v->mode == qkn::MODE_STATS)) && v->mode != qkn::MODE_HEAD)
     rpw = slots == 1 ? 4 : 2;
-  else if (v->mode == qkn::MODE_FWD && v->dtype == QKNORM_FP8_E4M3 && v->nt && slots <= 8 &&
-           a->T * nseg < 8 * simds)
-    rpw = 2;
   if (rpw == 1) return;
   v->rpw = rpw;
   for (int i = 0; i < nseg; ++i) {
@@ -479,33 +473,34 @@ void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nse
 
 // Paired rows: a forward launch of two segments whose rows are each one
 // slice in one wavefront (with staged weights) gives each wavefront one
-// token's row of both, when that makes 1.75 to 4 paired wavefronts per SIMD.
-// A workgroup then stores only after both of its rows have arrived, so the
-// launch issues nearly all its reads before its writes, where separate
+// token's row of both, up to 4 paired wavefronts per SIMD (one-wavefront
+// rows of both tensors already mean at least one; FP8 rows from 2). A
+// workgroup then stores only after all four tokens' rows have arrived, so
+// the launch issues nearly all its reads before its writes, where separate
 // wavefronts let the narrower rows' stores start while most rows are still
 // being read; reads and writes mixed in HBM cost more than either alone (24
-// MiB each way: 4.99 us read only, 4.78 us write only, 9.87 us as one copy).
-// MI355X, gated back to back, bit for bit the unpaired results, against the
-// unpaired launch: C4 (2048 x 5120/1024 bf16) 9.49 -> 8.95 us; 2048 x
-// 4096/1024 8.51 -> 7.59; 1792 x 4096/4096 12.53 -> 11.09; 3072 x 2048/512
-// 6.81 -> 6.30; fp32 2048 x 2048/512 8.99 -> 8.31. Outside the band it loses:
-// with fewer wavefronts than about two per SIMD the pair's longer chain is
-// exposed (1536 x 4096/4096: 9.90 -> 10.60), and from about five per SIMD
-// the other wavefronts already overlap each row's chain (8192 x 5120/1024:
-// 33.7 -> 34.5). FP8 rows keep their own single-round rule (two rows of one
-// tensor per wavefront): pairing them is within +-3% of it at 2048 tokens.
-bool pair_band(int64_t T, int num_cus) {
+// MiB each way: 4.99 us read only, 4.78 us write only, 9.87 us as one
+// copy). MI355X, gated back to back, bit for bit the unpaired results,
+// against the same launch unpaired: C4 (2048 x 5120/1024 bf16) 9.77 -> 8.68
+// us; 1792 x 4096/4096 12.49 -> 10.55; 4096 x 2048/512 9.05 -> 8.42; fp32
+// 2048 x 2048/512 8.89 -> 7.40; FP8 3072 x 5120/1024 8.98 -> 8.32, C4-fp8
+// 6.45 (two rows of one tensor per wavefront) -> 6.34. From about five per
+// SIMD the other wavefronts already overlap each row's chain and pairing
+// mostly loses (8192 x 4096/1024: 28.5 -> 29.4; FP8 6144 x 5120/1024: 15.1
+// -> 16.7); FP8 rows below two per SIMD run best unpaired (1536 x
+// 4096/4096: 6.33 against 7.04).
+bool pair_band(int64_t T, int num_cus, int dtype) {
   const int64_t simds = int64_t{4} * num_cus;
-  return 4 * T >= 7 * simds && T <= 4 * simds;
+  return T <= 4 * simds && (dtype != QKNORM_FP8_E4M3 || T >= 2 * simds);
 }
 void pair_rows(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
   v->pair = false;
-  if (nseg != 2 || v->mode != qkn::MODE_FWD || v->dtype == QKNORM_FP8_E4M3 || v->nw != 4 || v->narrow || !v->nt ||
-      v->pipe || ctx->opt.max_workgroups > 0 || ctx->opt.waves_per_row != 0)
+  if (nseg != 2 || v->mode != qkn::MODE_FWD || v->nw != 4 || v->narrow || !v->nt || v->pipe ||
+      ctx->opt.max_workgroups > 0 || ctx->opt.waves_per_row != 0)
     return;
   for (int i = 0; i < 2; ++i)
     if (a->seg[i].wpr_log2 != 0 || a->seg[i].lay_k != 1 || !a->seg[i].lds_gamma) return;
-  if (!pair_band(a->T, ctx->num_cus)) return;
+  if (!pair_band(a->T, ctx->num_cus, v->dtype)) return;
   if (a->seg[1].nslot > a->seg[0].nslot) {  // segment 0 is the wider
     const qkn::Seg t = a->seg[0];
     a->seg[0] = a->seg[1];

@@ -899,7 +899,7 @@ __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int 
   }
   // FP8 forward: when the weights alone bound every result inside the range
   // (checked once for all the wavefront's rows), the rows skip the
-  // per-vector test. With a single round of wavefronts this is faster.
+  // per-vector test.
   bool check = E::kSaturates;
   if constexpr (E::kSaturates && MODE == MODE_FWD) check = !E::weights_bound(g, s.h);
   if (check) {
@@ -1037,12 +1037,14 @@ __device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave
   wait_gamma_copies<VA + VB>();
   gamma_read_lds<E, VA>(ga, sa, La, lds_g);
   gamma_read_lds<E, VB>(gb, sb, Lb, lds_b);
-  // both statistics before any store: the wavefront writes only after all
-  // its reads have landed (the scheduling barrier keeps the compiler from
-  // moving the narrow row's stores up between them)
+  // both statistics before any store, and the workgroup's barrier before
+  // its first store: the workgroup writes only after all four tokens' rows
+  // have landed (the scheduling barrier keeps the compiler from moving the
+  // narrow row's stores up between the statistics)
   const float Sb = row_stat<E, VB, false>(db, sb, Lb, wave, lane, part, false);
   const float Sa = row_stat<E, VA, false>(da, sa, La, wave, lane, part, false);
   __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
   scale_store<E, VB, NT>(db, gb, Sb, sb, row, live, Lb);
   scale_store<E, VA, NT>(da, ga, Sa, sa, row, live, La);
 }

@@ -202,16 +202,16 @@ inline int compiled_vpl(int slots, int nw, int dtype) {
 //  - slot counts: those of kVpl4 / kVpl16 up to the type's register cap;
 //  - several rows per wavefront (rpw 2 or 4): 4-wavefront workgroups of
 //    whole-wavefront sub-teams, streaming, unpipelined; rows of 1 slot (4
-//    rows, every mode but the headwise one), statistics-only passes over
-//    rows of 2 slots (2 rows), or FP8 forward passes with 2 rows;
+//    rows, every mode but the headwise one), or statistics-only passes over
+//    rows of 2 slots (2 rows);
 //  - the persistent pipelined body: forward passes in 4-wavefront
 //    workgroups;
 //  - narrow-slice kernels stream (nt) and never serve the headwise form or
 //    the split path's apply step, whose layouts hold one slice;
 //  - ordinary cached row accesses (nt off): forward passes only;
-//  - paired rows (both segments' rows of a token in one wavefront): fp32 and
-//    bf16 forward passes in 4-wavefront workgroups, streaming, one row of each
-//    segment per wavefront, the second on the chain vpl, vpl/2, ...
+//  - paired rows (both segments' rows of a token in one wavefront): forward
+//    passes in 4-wavefront workgroups, streaming, one row of each segment per
+//    wavefront, the second on the chain vpl, vpl/2, ...
 constexpr bool compiled_vpl_value(int vpl, int nw, int dtype) {
   if (vpl < 1 || vpl > max_slots(dtype, nw)) return false;
   if (nw == 4) {
@@ -227,12 +227,10 @@ constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool 
                         int pair_b = 0) {
   if (!compiled_vpl_value(vpl, nw, dtype)) return false;
   if (pair_b != 0)
-    return mode == MODE_FWD && dtype != QKNORM_FP8_E4M3 && nw == 4 && !narrow && nt && !pipe && rpw == 1 &&
-           on_halving_chain(vpl, pair_b);
+    return mode == MODE_FWD && nw == 4 && !narrow && nt && !pipe && rpw == 1 && on_halving_chain(vpl, pair_b);
   if (rpw != 1) {
     if (nw != 4 || narrow || !nt || pipe) return false;
-    return (vpl == 1 && rpw == 4 && mode != MODE_HEAD) || (mode == MODE_STATS && vpl == 2 && rpw == 2) ||
-           (mode == MODE_FWD && dtype == QKNORM_FP8_E4M3 && rpw == 2);
+    return (vpl == 1 && rpw == 4 && mode != MODE_HEAD) || (mode == MODE_STATS && vpl == 2 && rpw == 2);
   }
   if (narrow && !nt) return false;
   if (pipe && (mode != MODE_FWD || nw != 4)) return false;

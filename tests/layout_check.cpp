@@ -251,7 +251,7 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
     for (int i = 0; i < nseg; ++i) a.seg[i] = seg[i];
     pair_rows(&ctx, &v, &a, nseg);
     CHECK(!v.pair || mode == qkn::MODE_FWD, "%s paired rows in mode %d", what, mode);
-    CHECK(!v.pair || (forced_wpr == 0 && pair_band(T, 256) && dtype != QKNORM_FP8_E4M3 && qkn::compiled(v)),
+    CHECK(!v.pair || (forced_wpr == 0 && pair_band(T, 256, dtype) && qkn::compiled(v)),
           "%s paired launch T=%lld", what, (long long)T);
     if (!v.pair) rows_per_wave(&ctx, &v, &a, nseg);
     for (int i = 0; i < nseg; ++i) {
@@ -261,9 +261,7 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
             a.seg[i].nwg);
       CHECK(v.rpw == 1 || (a.seg[i].wpr_log2 == 0 && !narrow && nw == 4 &&
                            ((mode == qkn::MODE_STATS && a.seg[i].nslot * v.rpw <= 4) ||
-                            (a.seg[i].nslot == 1 && v.rpw == 4) ||
-                            (mode == qkn::MODE_FWD && dtype == QKNORM_FP8_E4M3 && v.rpw == 2 &&
-                             a.seg[i].nslot <= 8))),
+                            (a.seg[i].nslot == 1 && v.rpw == 4))),
             "%s mode %d rpw %d with wpr_log2 %d, %d slots", what, mode, v.rpw, a.seg[i].wpr_log2, a.seg[i].nslot);
     }
   }

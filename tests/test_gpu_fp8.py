@@ -251,6 +251,52 @@ def test_fp8_dense_saturation(in_place, K, opts):
     assert_parity(yk[keep_k], rk, FP8, "k")
 
 
+@pytest.mark.parametrize("T,Hq,Hk,case", [
+    (2048, 5120, 1024, "plain"),        # C4-fp8's shape
+    (3001, 1024, 4096, "in_place"),     # key rows wider (the segments swap), T not a multiple of 4
+    (2048, 4096, 4096, "plain"),
+    (2560, 5120, 1024, "saturating"),   # weights of +-(200..600), a NaN and a zero row, in place
+])
+def test_fp8_paired_rows(T, Hq, Hk, case):
+    """FP8 forward launches of 2 to 4 paired wavefronts per SIMD (each
+    wavefront takes one token's query and key row): parity, and bit equality
+    with the same launch unpaired (a forced team of one wavefront), also when
+    rows saturate and are encoded again with the clamp from the input."""
+    q = rows(T, Hq, [61, T], dist="laplace")
+    k = rows(T, Hk, [62, T])
+    gq, gk = weights(Hq, 63), weights(Hk, 64)
+    keep = list(range(T))
+    if case == "saturating":
+        q, k = q.float(), k.float()
+        q[5, 333] = float("nan")
+        q[6] = 0.0
+        q, k = q.to(FP8), k.to(FP8)
+        gq, gk = weights(Hq, 65, 200.0, 600.0).float(), weights(Hk, 66, 200.0, 600.0).float()
+        gq[::3] = -gq[::3]
+        gq, gk = gq.to(torch.bfloat16), gk.to(torch.bfloat16)
+        keep = [t for t in range(T) if t != 5]
+    rq, _ = oracle.forward(q[keep], gq, 1e-6, 1)
+    rk, _ = oracle.forward(k, gk, 1e-6, 1)
+    if case == "saturating":
+        assert (np.abs(rq) >= 464).mean() > 0.05 and (np.abs(rk) >= 464).mean() > 0.05
+    say("fp8 paired rows", T, Hq, Hk, case)
+    outs = []
+    for ctx in (None, qk.Context(0, waves_per_row=1)):
+        dq, dk = gpu(q), gpu(k)
+        in_place = case != "plain"
+        yq, yk = qk.forward(dq, dk, gpu(gq), gpu(gk), eps=1e-6, ctx=ctx,
+                            out_q=dq if in_place else None, out_k=dk if in_place else None)
+        torch.cuda.synchronize()
+        outs.append((yq.view(torch.uint8).cpu(), yk.view(torch.uint8).cpu(), yq, yk))
+    (bq, bk, yq, yk), (bq1, bk1, _, _) = outs
+    assert torch.equal(bq, bq1) and torch.equal(bk, bk1)
+    if case == "saturating":
+        hq = yq.cpu().float()
+        assert torch.isnan(hq[5]).all() and (hq[6] == 0).all()
+    assert_parity(yq[keep], rq, FP8, "q")
+    assert_parity(yk, rk, FP8, "k")
+
+
 def test_fp8_packed_qkv_in_place():
     T, Hq, Hk, Hv = 45, 2048, 512, 512
     H = Hq + Hk + Hv

@@ -24,7 +24,7 @@ WORKLOAD_PLANS = [
     'plan c4 K=1: nw=4 body=10 narrow=0 rows_per_wave=1 paired=2 | q team=1 sub_lanes=64 slots=10 masked=0 | k team=1 sub_lanes=64 slots=2 masked=0',
     'plan c5 K=8: nw=4 body=4 narrow=0 rows_per_wave=1 paired=0 | q team=2 sub_lanes=64 slots=4 masked=0 | k team=2 sub_lanes=64 slots=4 masked=0',
     'plan c5 K=1: nw=4 body=4 narrow=0 rows_per_wave=1 paired=0 | q team=2 sub_lanes=128 slots=4 masked=0 | k team=2 sub_lanes=128 slots=4 masked=0',
-    'plan c4f8 K=1: nw=4 body=5 narrow=0 rows_per_wave=2 paired=0 | q team=1 sub_lanes=64 slots=5 masked=0 | k team=1 sub_lanes=64 slots=1 masked=0',
+    'plan c4f8 K=1: nw=4 body=5 narrow=0 rows_per_wave=1 paired=1 | q team=1 sub_lanes=64 slots=5 masked=0 | k team=1 sub_lanes=64 slots=1 masked=0',
     'plan c5f8 K=8: nw=4 body=4 narrow=1 rows_per_wave=1 paired=0 | q team=1 sub_lanes=8 slots=4 masked=0 | k team=1 sub_lanes=8 slots=4 masked=0',
     'plan c5f8 K=1: nw=4 body=4 narrow=0 rows_per_wave=1 paired=0 | q team=1 sub_lanes=64 slots=4 masked=0 | k team=1 sub_lanes=64 slots=4 masked=0',
 ]
