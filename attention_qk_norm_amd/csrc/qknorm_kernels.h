@@ -329,7 +329,7 @@ struct Hot {
   float* stats_out;
   int64_t x_stride, y_stride, T;
   int rows_per_wg, nwg, nslot, wpr_log2, sub_lanes_log2, lds_gamma, lay_k, comb_k, masked, slice_vec,
-      head_log2, emit_rinv, dense, tail_lanes, lds_gamma_vec;
+      head_log2, emit_rinv, dense, tail_lanes;
   uint32_t row_bytes, flush_mask;
   float inv_slice_vec, h, inv_h, eps;
 
@@ -338,7 +338,7 @@ struct Hot {
         x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
         nslot(s.nslot), wpr_log2(s.wpr_log2), sub_lanes_log2(s.sub_lanes_log2), lds_gamma(s.lds_gamma),
         lay_k(s.lay_k), comb_k(s.comb_k), masked(s.masked), slice_vec(s.slice_vec), head_log2(s.head_log2),
-        emit_rinv(s.emit_rinv), dense(s.dense), tail_lanes(s.tail_lanes), lds_gamma_vec(s.lds_gamma_vec),
+        emit_rinv(s.emit_rinv), dense(s.dense), tail_lanes(s.tail_lanes),
         row_bytes(s.row_bytes), flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h),
         inv_h(s.inv_h), eps(a.eps) {}
 
@@ -1012,16 +1012,17 @@ __device__ __forceinline__ void dispatch(const Hot& s, const Tables<VPL>& tb, in
 // workgroup stages both weight vectors in LDS (b's after a's). Every row load
 // goes out before the first wait, and each row is finished exactly as on its
 // own (the same strided layout, the same order of operations, so the same
-// bits). Launches of one or a few rounds of wavefronts then issue all their
-// reads before nearly any write: a workgroup stores only after both of its
-// rows have arrived, where separate wavefronts for the two segments let the
-// narrow rows' stores start while most rows are still being read.
+// bits). Launches of one or a few rounds of wavefronts then issue nearly all
+// their reads before their writes: a workgroup stores only after all its
+// tokens' rows have arrived (a barrier precedes its first store), where
+// separate wavefronts for the two segments let the narrow rows' stores start
+// while most rows are still being read.
 template <class E, int VA, int VB, int NW, bool NT>
 __device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave, int lane, float* part,
                                           u32x4* lds_g) {
   const Layout<VA> La(wave, lane);
   const Layout<VB> Lb(wave, lane);
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * NW + wave;
   const bool live = row < sa.T;
   u32x4 da[VA], db[VB];
   typename E::G ga[VA], gb[VB];
@@ -1038,7 +1039,7 @@ __device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave
   gamma_read_lds<E, VA>(ga, sa, La, lds_g);
   gamma_read_lds<E, VB>(gb, sb, Lb, lds_b);
   // both statistics before any store, and the workgroup's barrier before
-  // its first store: the workgroup writes only after all four tokens' rows
+  // its first store: the workgroup writes only after all its tokens' rows
   // have landed (the scheduling barrier keeps the compiler from moving the
   // narrow row's stores up between the statistics)
   const float Sb = row_stat<E, VB, false>(db, sb, Lb, wave, lane, part, false);

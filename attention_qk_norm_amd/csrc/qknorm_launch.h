@@ -80,7 +80,9 @@ struct Seg {
   int32_t dense;          // 1: no slot needs a lane test (see slot_offset)
   int32_t tail_lanes;     // lanes of the last slot of each slice (the ragged slot when not dense)
   int32_t lds_gamma_vec;  // paired launches: where this segment's staged gamma starts in LDS
-                          // (16-byte vectors; 0 for segment 0)
+                          // (16-byte vectors; 0 for segment 0). The host sizes LDS by it
+                          // and the layout checker compares it with the offset the kernel
+                          // derives from segment 0's row bytes.
   int32_t slot_base[kMaxSlots];
   int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
   int32_t pad_[13];             // whole 64-byte lines per segment
