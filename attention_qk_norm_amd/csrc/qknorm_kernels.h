@@ -329,7 +329,7 @@ struct Hot {
   float* stats_out;
   int64_t x_stride, y_stride, T;
   int rows_per_wg, nwg, nslot, wpr_log2, sub_lanes_log2, lds_gamma, lay_k, comb_k, masked, slice_vec,
-      head_log2, emit_rinv, dense, tail_lanes;
+      head_log2, emit_rinv, dense, tail_lanes, pack_log2;
   uint32_t row_bytes, flush_mask;
   float inv_slice_vec, h, inv_h, eps;
 
@@ -338,7 +338,7 @@ struct Hot {
         x_stride(s.x_stride), y_stride(s.y_stride), T(a.T), rows_per_wg(s.rows_per_wg), nwg(s.nwg),
         nslot(s.nslot), wpr_log2(s.wpr_log2), sub_lanes_log2(s.sub_lanes_log2), lds_gamma(s.lds_gamma),
         lay_k(s.lay_k), comb_k(s.comb_k), masked(s.masked), slice_vec(s.slice_vec), head_log2(s.head_log2),
-        emit_rinv(s.emit_rinv), dense(s.dense), tail_lanes(s.tail_lanes),
+        emit_rinv(s.emit_rinv), dense(s.dense), tail_lanes(s.tail_lanes), pack_log2(s.pack_log2),
         row_bytes(s.row_bytes), flush_mask(s.flush_mask), inv_slice_vec(s.inv_slice_vec), h(s.h),
         inv_h(s.inv_h), eps(a.eps) {}
 
@@ -927,6 +927,111 @@ __device__ __forceinline__ void body_rows(const Hot& s, const Layout<V>& L, int 
   }
 }
 
+// Packed rows: rows of one slice and at most 32 vectors, SLOTS slots per
+// wavefront and 64 / 2^hl rows in each, row i of a slot over the aligned
+// lanes i * 2^hl ... (lane l holds the row's vector l mod 2^hl; 2^hl is the
+// row's vector count rounded up to a power of two), so no lane idles where
+// one row per slot would leave most of the wavefront empty. A row's squares
+// are summed over its lane group by the same butterfly steps a whole
+// wavefront starts with; in the one-row layout the further steps only add
+// the empty lanes' zeros, so the statistic, and everything computed from it,
+// has the same bits. The weights are each lane's one vector, the same in
+// every slot. A wavefront's rows share one buffer resource spanning them; a
+// lane's offset adds its row's distance from the first (the host keeps the
+// span below 2^31 bytes).
+template <class E, int NW, int MODE, bool NT, int SLOTS>
+__device__ __forceinline__ void body_packed(const Hot& s, int wave, int lane) {
+  const int hl = s.pack_log2;
+  const int rps_log2 = 6 - hl;  // rows per slot
+  const int sub = lane >> hl;   // the lane's row within a slot
+  const int vec = lane & ((1 << hl) - 1);
+  const bool vlive = static_cast<uint32_t>(vec) < (s.row_bytes >> 4);
+  const int64_t xs = s.x_stride * E::kBytes, ys = s.y_stride * E::kBytes;
+  typename E::G g[1];
+  if constexpr (MODE != MODE_STATS)
+    g[0] = E::load_gamma(rsrc(s.gamma, s.row_bytes * E::kGammaScale),
+                         vlive ? static_cast<uint32_t>(vec) * 16u : kOutside);
+  // FP8: the weight bound, as for one-row layouts (forward passes only)
+  bool check = E::kSaturates;
+  if constexpr (E::kSaturates && MODE == MODE_FWD) check = !E::weights_bound(g, s.h);
+  for (int64_t gi = blockIdx.x; gi < s.nwg; gi += gridDim.x) {
+    const int64_t row0 = ((gi * NW + wave) * SLOTS) << rps_log2;
+    int64_t span = s.T - row0;  // rows of this wavefront
+    span = span < (int64_t{SLOTS} << rps_log2) ? span : (int64_t{SLOTS} << rps_log2);
+    int64_t row[SLOTS];
+    uint32_t xo[SLOTS], yo[SLOTS];
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      const int64_t rel = (int64_t{j} << rps_log2) + sub;
+      row[j] = row0 + rel;
+      xo[j] = packed_offset(rel, span, vec, vlive, xs);
+      yo[j] = packed_offset(rel, span, vec, vlive, ys);
+    }
+    const auto xr = rsrc(static_cast<const char*>(s.x) + row0 * xs, packed_bytes(span, xs, s.row_bytes));
+    u32x4 d[SLOTS];
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) d[j] = load16<NT>(xr, xo[j]);
+    float S[SLOTS];
+    if constexpr (MODE == MODE_APPLY) {
+      // lane v of a row's group fetches the row's partial v (the host packs
+      // apply launches only where a group has a lane for each partial), and
+      // the partials are added in ascending order from zero, partial k read
+      // from the group's lane k
+      float pk[SLOTS];
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j)
+        pk[j] = (vec < s.comb_k && row[j] < s.T) ? s.stats_in[vec * s.T + row[j]] : 0.f;
+      const int group = (sub << hl) * 4;  // ds_bpermute address of the group's first lane
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j) S[j] = 0.f;
+      for (int k = 0; k < s.comb_k; ++k) {
+#pragma unroll
+        for (int j = 0; j < SLOTS; ++j)
+          S[j] += __int_as_float(__builtin_amdgcn_ds_bpermute(group + 4 * k, __float_as_int(pk[j])));
+      }
+    } else {
+      float q[SLOTS];
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j) q[j] = E::sumsq(d[j], 0.f);
+      head_sums<SLOTS>(q, hl, lane);
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j) S[j] = 0.f + q[j];
+    }
+    if constexpr (MODE == MODE_STATS) {
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j)
+        if (vec == 0 && row[j] < s.T) s.stats_out[row[j]] = s.emit_rinv ? inv_rms(S[j], s.inv_h, s.eps) : S[j];
+    } else {
+      const auto yr = rsrc(static_cast<char*>(s.y) + row0 * ys, packed_bytes(span, ys, s.row_bytes));
+      uint32_t redo = 0;
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j) {
+        const float r = inv_rms(S[j], s.inv_h, s.eps);
+        float peak = 0.f;
+        const u32x4 o = E::template encode<false>(d[j], g[0], r, peak);
+        if (E::kSaturates && check) {
+          // as encode_store: a vector with a result past the range is stored
+          // again, from the input, with the clamp
+          const bool over = peak > 448.0f;
+          redo |= over ? 1u << j : 0u;
+          store16<NT>(yr, over ? kOutside : yo[j], o);
+        } else {
+          store16<NT>(yr, yo[j], o);
+        }
+      }
+      if (E::kSaturates && redo != 0) {
+        for (int j = 0; j < SLOTS; ++j) {
+          if ((redo >> j) & 1u) {
+            float unused = 0.f;
+            const u32x4 x = load16<NT>(xr, xo[j]);
+            store16<NT>(yr, yo[j], E::template encode<true>(x, g[0], inv_rms(S[j], s.inv_h, s.eps), unused));
+          }
+        }
+      }
+    }
+  }
+}
+
 template <class E, int V, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW>
 __device__ __forceinline__ void body(const Hot& s, const Tables<VPL>& tb, int wave, int lane, float* part,
                                      u32x4* lds_g) {
@@ -1053,13 +1158,19 @@ __device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave
 // blockIdx.y selects the segment (query rows, key rows), so everything a
 // wavefront needs from the kernel arguments is one round of scalar loads;
 // a paired launch reads both segments in that round.
-template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW = 1, int PAIRB = 0>
+template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW = 1, int PAIRB = 0,
+          bool PACK = false>
 __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   __shared__ float part[NW * kWave];  // per-wavefront slice partials (teams of > 1 wave)
   extern __shared__ u32x4 lds_g[];    // staged gamma (dynamic size: the launch's widest row)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-  if constexpr (PAIRB > 0) {
+  if constexpr (PACK) {
+    static_assert(VPL == 1 && NW == 4 && !NARROW && NT && !PIPE && RPW == kPackSlots && PAIRB == 0,
+                  "packed rows: one 4-slot body");
+    const Hot s(a, a.seg[blockIdx.y]);
+    body_packed<E, NW, MODE, NT, RPW>(s, wave, lane);
+  } else if constexpr (PAIRB > 0) {
     // paired rows: segment 1 runs the body of PAIRB slots (each pairing its
     // own kernel, so a narrow second row does not carry a wide one's registers)
     static_assert(MODE == MODE_FWD && NW == 4 && !NARROW && NT && !PIPE && RPW == 1, "paired forward rows only");
@@ -1078,11 +1189,12 @@ __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
 // The launch dispatch: the run-time variant picks one of the kernels the
 // compiled() table names; any other combination instantiates nothing and is
 // refused.
-template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW, int PAIRB = 0>
+template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW, int PAIRB = 0,
+          bool PACK = false>
 hipError_t launch_one(const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
-  if constexpr (compiled(E::kDtype, MODE, VPL, NW, NARROW, NT, PIPE, RPW, PAIRB)) {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE, NARROW, NT, PIPE, RPW, PAIRB>), gd, dim3(NW * kWave), lds, st,
-                       a);
+  if constexpr (compiled(E::kDtype, MODE, VPL, NW, NARROW, NT, PIPE, RPW, PAIRB, PACK)) {
+    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE, NARROW, NT, PIPE, RPW, PAIRB, PACK>), gd, dim3(NW * kWave),
+                       lds, st, a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
@@ -1104,7 +1216,9 @@ hipError_t by_rpw(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStr
       return v.pair ? by_pair_b<E, VPL, NW, MODE, NARROW, NT, PIPE, VPL>(v, a, gd, lds, st)
                     : launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 1>(a, gd, lds, st);
     case 2: return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 2>(a, gd, lds, st);
-    case 4: return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 4>(a, gd, lds, st);
+    case 4:
+      return v.pack ? launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 4, 0, true>(a, gd, lds, st)
+                    : launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 4>(a, gd, lds, st);
     default: return hipErrorInvalidValue;
   }
 }

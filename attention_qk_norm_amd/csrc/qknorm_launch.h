@@ -25,6 +25,11 @@
 // of at most 64 vectors, so each head sits in one slot of one aligned group
 // of lanes of one wavefront, and lane l always holds the head's vector
 // l mod (vectors per head): its weights are the same in every slot.
+//
+// Packed rows: launches over many rows of one slice and at most 32 vectors
+// put 64 / 2^pack_log2 rows in each slot of a wavefront, row i of the slot
+// over the aligned lanes i * 2^pack_log2 ... (lane l holding vector
+// l mod 2^pack_log2), where one row per slot would leave lanes idle.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -85,7 +90,8 @@ struct Seg {
                           // derives from segment 0's row bytes.
   int32_t slot_base[kMaxSlots];
   int32_t slot_lim[kMaxSlots];  // 0 for j >= nslot
-  int32_t pad_[13];             // whole 64-byte lines per segment
+  int32_t pack_log2;            // packed launches: log2 of the lanes per row (rows of <= 32 vectors)
+  int32_t pad_[12];             // whole 64-byte lines per segment
 };
 
 // T and eps lead, so that they share a 64-byte line with the first fields of
@@ -137,6 +143,21 @@ __host__ __device__ inline uint32_t slot_offset(int base, int lane_vec, int stl,
                                                     : kOutsideOffset;
 }
 
+// Packed rows: the byte offset of a lane's vector in one slot, from the
+// wavefront's first row (`rel`: the slot's first row plus the lane's row
+// within the slot), or kOutsideOffset when the lane holds nothing there (a
+// vector past the row, or a row past the `span` rows the wavefront has); and
+// the byte length of the buffer resource over the wavefront's rows. Used by
+// the kernels and by the host-side layout checks.
+__host__ __device__ inline uint32_t packed_offset(int64_t rel, int64_t span, int vec, bool vlive,
+                                                  int64_t stride_bytes) {
+  return (vlive && rel < span) ? static_cast<uint32_t>(rel * stride_bytes) + static_cast<uint32_t>(vec) * 16u
+                               : kOutsideOffset;
+}
+__host__ __device__ inline uint32_t packed_bytes(int64_t span, int64_t stride_bytes, uint32_t row_bytes) {
+  return span > 0 ? static_cast<uint32_t>((span - 1) * stride_bytes) + row_bytes : 0u;
+}
+
 // Compile-time variants a launch picks from.
 struct Variant {
   int dtype;     // qknorm_dtype
@@ -151,7 +172,12 @@ struct Variant {
   bool pair = false;  // FWD: each wavefront takes one token's row of both segments
                       // (segment 0 the wider), grid.y = 1
   int vpl_b = 0;      // paired: the body for segment 1's rows, on the chain vpl, vpl/2, ...
+  bool pack = false;  // FWD, STATS, APPLY: rows of one slice and <= 32 vectors, several
+                      // per slot (kPackSlots slots per wavefront)
 };
+
+// Slots per wavefront of a packed launch; each holds 64 / 2^pack_log2 rows.
+constexpr int kPackSlots = 4;
 
 // The body for `nslot` slots in a kernel built for `vpl`: the smallest of
 // vpl, vpl/2, vpl/4, ... that holds them (the kernels' dispatch).
@@ -214,6 +240,9 @@ inline int compiled_vpl(int slots, int nw, int dtype) {
 //  - paired rows (both segments' rows of a token in one wavefront): forward
 //    passes in 4-wavefront workgroups, streaming, one row of each segment per
 //    wavefront, the second on the chain vpl, vpl/2, ...
+//  - packed rows (several narrow rows in each slot): forward, statistics and
+//    apply passes in 4-wavefront workgroups, streaming, one slot per row,
+//    kPackSlots slots per wavefront.
 constexpr bool compiled_vpl_value(int vpl, int nw, int dtype) {
   if (vpl < 1 || vpl > max_slots(dtype, nw)) return false;
   if (nw == 4) {
@@ -226,8 +255,11 @@ constexpr bool compiled_vpl_value(int vpl, int nw, int dtype) {
   return false;
 }
 constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool nt, bool pipe, int rpw,
-                        int pair_b = 0) {
+                        int pair_b = 0, bool pack = false) {
   if (!compiled_vpl_value(vpl, nw, dtype)) return false;
+  if (pack)
+    return (mode == MODE_FWD || mode == MODE_STATS || mode == MODE_APPLY) && vpl == 1 && nw == 4 && !narrow && nt &&
+           !pipe && rpw == kPackSlots && pair_b == 0;
   if (pair_b != 0)
     return mode == MODE_FWD && nw == 4 && !narrow && nt && !pipe && rpw == 1 && on_halving_chain(vpl, pair_b);
   if (rpw != 1) {
@@ -241,7 +273,7 @@ constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool 
   return true;
 }
 inline bool compiled(const Variant& v) {
-  return compiled(v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0);
+  return compiled(v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0, v.pack);
 }
 
 // Enqueue one launch: grid.x workgroups per segment, grid.y segments, with

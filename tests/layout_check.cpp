@@ -43,12 +43,13 @@ static Variant g_v;
 static Args g_a;
 static dim3 g_grid;
 static unsigned g_lds;
-using VariantKey = std::tuple<int, int, int, int, bool, bool, bool, int, int>;
+using VariantKey = std::tuple<int, int, int, int, bool, bool, bool, int, int, bool>;
 static VariantKey key(const Variant& v) {
-  return VariantKey{v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0};
+  return VariantKey{v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0, v.pack};
 }
-static long g_paired;
+static long g_paired, g_packed, g_packed_covered;
 static void check_pair_launch(const Variant& v, const Args& a, dim3 grid, unsigned lds);
+static void check_pack_launch(const Variant& v, const Args& a, dim3 grid, unsigned lds);
 static std::set<VariantKey> g_reached;
 static long g_launches, g_uncompiled;
 hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes, hipStream_t) {
@@ -59,10 +60,12 @@ hipError_t launch(const Variant& v, const Args& a, dim3 grid, unsigned lds_bytes
   g_reached.insert(key(v));
   ++g_launches;
   if (v.pair) check_pair_launch(v, a, grid, lds_bytes);
+  if (v.pack) check_pack_launch(v, a, grid, lds_bytes);
   if (!compiled(v)) {
     if (g_uncompiled < 10)
-      std::printf("FAIL no kernel for reached variant dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d\n",
-                  v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw);
+      std::printf("FAIL no kernel for reached variant dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d "
+                  "pack=%d\n",
+                  v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pack);
     ++g_uncompiled;
     return hipErrorInvalidValue;
   }
@@ -132,6 +135,80 @@ void qkn::check_pair_launch(const Variant& v, const Args& a, dim3 grid, unsigned
     const int64_t gvec = gamma_bytes(a.seg[i].row_bytes, v.dtype) / 16;
     CHECK(gvec <= int64_t{(body + 1) / 2} * 4 * 64 * (v.dtype == QKNORM_FP8_E4M3 ? 2 : 1),
           "paired segment %d: %lld weight vectors past the copy loop of body %d", i, (long long)gvec, body);
+  }
+}
+
+// A packed launch (several narrow rows per slot): every segment one slice
+// of at most 32 vectors in one-wavefront teams, 2^pack_log2 lanes per row
+// (the vector count, or in apply launches the partials if more, rounded up
+// to a power of two), no staged weights, the
+// workgroups covering all rows, and a wavefront's rows within one buffer
+// resource. For up to 20001 rows, the kernel's index arithmetic is run for
+// every workgroup, wavefront, slot and lane: each (row, vector) is held by
+// exactly one lane, every live offset lies inside the wavefront's resource
+// and points at that vector, and every other lane's offset is dropped.
+void qkn::check_pack_launch(const Variant& v, const Args& a, dim3 grid, unsigned lds) {
+  ++g_packed;
+  CHECK((v.mode == MODE_FWD || v.mode == MODE_STATS || v.mode == MODE_APPLY) && v.nw == 4 && v.vpl == 1 &&
+            !v.narrow && v.nt && !v.pipe && v.rpw == kPackSlots && !v.pair,
+        "packed variant mode %d", v.mode);
+  CHECK(lds == 0, "packed launch with %u bytes of LDS", lds);
+  const int nseg = static_cast<int>(grid.y);
+  CHECK(nseg == 1 || nseg == 2, "packed grid.y %u", grid.y);
+  const int64_t T = a.T;
+  const int eb = elem_bytes(v.dtype);
+  for (int i = 0; i < nseg; ++i) {
+    const Seg& s = a.seg[i];
+    const int64_t nvec = s.row_bytes / 16;
+    const int hl = s.pack_log2;
+    CHECK(s.wpr_log2 == 0 && s.sub_lanes_log2 == 6 && !s.masked && s.lay_k == 1 && s.nslot == 1 && !s.lds_gamma &&
+              s.rpw == kPackSlots && s.rows_per_wg == 4,
+          "packed segment %d layout", i);
+    // a group: the row's vectors, and in apply launches a lane per partial
+    const int64_t lanes = v.mode == MODE_APPLY && s.comb_k > nvec ? s.comb_k : nvec;
+    CHECK(nvec >= 1 && nvec <= 32 && hl >= 0 && hl <= 5 && (int64_t{1} << hl) >= lanes &&
+              (hl == 0 || (int64_t{1} << (hl - 1)) < lanes),
+          "packed segment %d: %lld vectors (%d partials) in groups of 2^%d lanes", i, (long long)nvec, s.comb_k, hl);
+    const int64_t per_wave = int64_t{kPackSlots} << (6 - hl), per_wg = 4 * per_wave;
+    CHECK(int64_t{s.nwg} * per_wg >= T && int64_t{s.nwg - 1} * per_wg < T && grid.x >= unsigned(s.nwg),
+          "packed segment %d: %d workgroups of %lld rows for T=%lld, grid %u", i, s.nwg, (long long)per_wg,
+          (long long)T, grid.x);
+    const int64_t xs = s.x_stride * eb, ys = s.y_stride * eb;
+    CHECK((per_wave - 1) * xs + s.row_bytes < (int64_t{1} << 31), "packed segment %d: input span", i);
+    CHECK(v.mode == MODE_STATS || (per_wave - 1) * ys + s.row_bytes < (int64_t{1} << 31),
+          "packed segment %d: output span", i);
+    if (T > 20001) continue;
+    ++g_packed_covered;
+    std::vector<unsigned char> held(static_cast<size_t>(T * nvec), 0);
+    for (int64_t gi = 0; gi < s.nwg; ++gi)
+      for (int wave = 0; wave < 4; ++wave) {
+        const int64_t row0 = ((gi * 4 + wave) * kPackSlots) << (6 - hl);
+        int64_t span = T - row0;
+        span = span < per_wave ? span : per_wave;
+        const uint32_t xbytes = packed_bytes(span, xs, s.row_bytes), ybytes = packed_bytes(span, ys, s.row_bytes);
+        for (int j = 0; j < kPackSlots; ++j)
+          for (int lane = 0; lane < 64; ++lane) {
+            const int sub = lane >> hl, vec = lane & ((1 << hl) - 1);
+            const bool vlive = vec < nvec;
+            const int64_t rel = (int64_t{j} << (6 - hl)) + sub, row = row0 + rel;
+            const uint32_t xo = packed_offset(rel, span, vec, vlive, xs);
+            const uint32_t yo = packed_offset(rel, span, vec, vlive, ys);
+            if (vlive && row < T) {
+              CHECK(xo == static_cast<uint32_t>(rel * xs + 16 * vec) && xo + 16 <= xbytes,
+                    "packed segment %d row %lld vector %d: input offset %u of %u", i, (long long)row, vec, xo, xbytes);
+              CHECK(v.mode == MODE_STATS ||
+                        (yo == static_cast<uint32_t>(rel * ys + 16 * vec) && yo + 16 <= ybytes),
+                    "packed segment %d row %lld vector %d: output offset %u of %u", i, (long long)row, vec, yo,
+                    ybytes);
+              ++held[static_cast<size_t>(row * nvec + vec)];
+            } else {
+              CHECK(xo == kOutsideOffset && yo == kOutsideOffset, "packed segment %d: empty lane not dropped", i);
+            }
+          }
+      }
+    for (size_t k = 0; k < held.size(); ++k)
+      CHECK(held[k] == 1, "packed segment %d: row %lld vector %lld held %d times", i,
+            (long long)(k / static_cast<size_t>(nvec)), (long long)(k % static_cast<size_t>(nvec)), held[k]);
   }
 }
 
@@ -218,7 +295,7 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
   bool narrow = false;
   for (int i = 0; i < nseg; ++i) narrow = narrow || narrow_plan(plans[i]);
   int slots = 0;
-  qkn::Seg seg[2];
+  qkn::Seg seg[2] = {};
   bool masked[2] = {false, false};
   char what[160];
   std::snprintf(what, sizeof what, "T=%lld hq=%lld hk=%lld K=%d wpr=%d dt=%d", (long long)T, (long long)hq,
@@ -226,6 +303,7 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
   for (int i = 0; i < nseg; ++i) {
     masked[i] = plans[i].masked;
     fill_layout(&seg[i], plans[i], nw, in[i].nvec, K, T);
+    seg[i].x_stride = seg[i].y_stride = i == 0 ? hq : hk;  // contiguous rows
     share_gamma(&seg[i], dtype);
     slots = seg[i].nslot > slots ? seg[i].nslot : slots;
     // the kernels for narrow slices tell the layouts apart by the masked
@@ -253,9 +331,16 @@ static void run_forward(int64_t T, int64_t hq, int64_t hk, int K, int forced_wpr
     CHECK(!v.pair || mode == qkn::MODE_FWD, "%s paired rows in mode %d", what, mode);
     CHECK(!v.pair || (forced_wpr == 0 && pair_band(T, 256, dtype) && qkn::compiled(v)),
           "%s paired launch T=%lld", what, (long long)T);
-    if (!v.pair) rows_per_wave(&ctx, &v, &a, nseg);
+    if (!v.pair) pack_rows(&ctx, &v, &a, nseg);
+    CHECK(!v.pack || (forced_wpr == 0 && K == 1 && T * nseg >= 16 * 1024 && qkn::compiled(v)),
+          "%s packed launch T=%lld", what, (long long)T);
+    if (v.pack) qkn::check_pack_launch(v, a, dim3(a.seg[0].nwg > a.seg[nseg - 1].nwg ? a.seg[0].nwg
+                                                                                      : a.seg[nseg - 1].nwg,
+                                                  nseg),
+                                       0);
+    if (!v.pair && !v.pack) rows_per_wave(&ctx, &v, &a, nseg);
     for (int i = 0; i < nseg; ++i) {
-      const int64_t per_wg = int64_t{a.seg[i].rows_per_wg} * a.seg[i].rpw;
+      const int64_t per_wg = int64_t{a.seg[i].rows_per_wg} * a.seg[i].rpw << (v.pack ? 6 - a.seg[i].pack_log2 : 0);
       CHECK(a.seg[i].rpw == v.rpw && (v.rpw == 1 || v.rpw == 2 || v.rpw == 4), "%s rpw %d", what, v.rpw);
       CHECK(int64_t{a.seg[i].nwg} * per_wg >= T && int64_t{a.seg[i].nwg - 1} * per_wg < T, "%s nwg %d", what,
             a.seg[i].nwg);
@@ -350,7 +435,8 @@ static void print_plan(const char* name, int dtype, int64_t T, int64_t hq, int64
   }
   qkn::Variant v{dtype, qkn::MODE_FWD, qkn::compiled_vpl(slots, nw, dtype), nw, narrow, true, false};
   pair_rows(&ctx, &v, &a, 2);
-  if (!v.pair) rows_per_wave(&ctx, &v, &a, 2);
+  if (!v.pair) pack_rows(&ctx, &v, &a, 2);
+  if (!v.pair && !v.pack) rows_per_wave(&ctx, &v, &a, 2);
   std::printf("plan %s: nw=%d body=%d narrow=%d rows_per_wave=%d paired=%d", name, nw, v.vpl, narrow ? 1 : 0, v.rpw,
               v.pair ? v.vpl_b : 0);
   for (int i = 0; i < 2; ++i)
@@ -476,19 +562,23 @@ int main() {
             for (int nt = 0; nt < 2; ++nt)
               for (int pipe = 0; pipe < 2; ++pipe)
                 for (int rpw : {1, 2, 4})
-                  for (int pb = 0; pb <= qkn::kMaxSlots; ++pb) {
-                    if (!qkn::compiled(dtype, mode, vpl, nw, narrow, nt, pipe, rpw, pb)) continue;
-                    ++compiled_n;
-                    const qkn::VariantKey k{dtype, mode, vpl, nw, narrow != 0, nt != 0, pipe != 0, rpw, pb};
-                    if (!qkn::g_reached.count(k)) unused.push_back(k);
-                  }
+                  for (int pb = 0; pb <= qkn::kMaxSlots; ++pb)
+                    for (int pk = 0; pk < 2; ++pk) {
+                      if (!qkn::compiled(dtype, mode, vpl, nw, narrow, nt, pipe, rpw, pb, pk != 0)) continue;
+                      ++compiled_n;
+                      const qkn::VariantKey k{dtype, mode, vpl, nw, narrow != 0, nt != 0, pipe != 0, rpw, pb,
+                                              pk != 0};
+                      if (!qkn::g_reached.count(k)) unused.push_back(k);
+                    }
   std::printf("entry points: %ld calls, %ld launches, %zu variants reached, %ld compiled, %zu compiled and "
               "never reached\n", calls, qkn::g_launches, qkn::g_reached.size(), compiled_n, unused.size());
+  std::printf("paired launches %ld; packed launches %ld, %ld segments traced lane by lane\n", qkn::g_paired,
+              qkn::g_packed, qkn::g_packed_covered);
   CHECK(unused.empty(), "%zu compiled variants that no call reaches", unused.size());
   for (const auto& k : unused)
-    std::printf("  unreached: dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d paired=%d\n",
+    std::printf("  unreached: dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d paired=%d packed=%d\n",
                 std::get<0>(k), std::get<1>(k), std::get<2>(k), std::get<3>(k), (int)std::get<4>(k),
-                (int)std::get<5>(k), (int)std::get<6>(k), std::get<7>(k), std::get<8>(k));
+                (int)std::get<5>(k), (int)std::get<6>(k), std::get<7>(k), std::get<8>(k), (int)std::get<9>(k));
   std::printf("%d cases, %d failures\n", cases, failures);
   return failures ? 1 : 0;
 }
