@@ -185,8 +185,8 @@ int qknorm_forward_headwise(qknorm_ctx *ctx, int dtype, int64_t T,
  *
  * S_t formed as qknorm_forward forms it (K slice partials added in
  * ascending order). The value is bit for bit the factor qknorm_forward
- * multiplies row t by: its output is (x * rinv) * gamma rounded once to the
- * output type.
+ * multiplies row t by: its output is (x * gamma) * rinv in fp32, rounded to
+ * the output type.
  *
  *   q, k        rows to read (only x, width and x_stride are used; k may be
  *               NULL)

@@ -538,9 +538,10 @@ def test_headwise_zero_heads_and_reproducibility():
 # ---- the per-token inverse RMS alone ------------------------------------------------
 
 def forward_from_rinv(x, r, g, dtype):
-    """(x * r) * gamma in fp32, rounded once to the output type: the fused
-    forward's arithmetic, given its factor r."""
-    y = (x.float() * r.cpu()[:, None]) * g.float()
+    """(x * gamma) * r in fp32, rounded once to the output type: the fused
+    forward's arithmetic, given its factor r (for bf16 rows x * gamma is
+    exact in fp32)."""
+    y = (x.float() * g.float()) * r.cpu()[:, None]
     return y.to(dtype)
 
 
