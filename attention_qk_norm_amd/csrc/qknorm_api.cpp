@@ -494,6 +494,16 @@ bool pair_band(int64_t T, int num_cus, int dtype) {
   const int64_t simds = int64_t{4} * num_cus;
   return T <= 4 * simds && (dtype != QKNORM_FP8_E4M3 || T >= 2 * simds);
 }
+// Paired FP8 rows form the products x gamma before the statistic when the
+// launch has at most 2 paired wavefronts per SIMD: those kernels hold 16
+// more VGPRs per slot and keep 2 or 3 wavefronts per SIMD. MI355X, gated
+// back to back, against the scaling after the statistic: 2048 tokens 6.47
+// -> 6.13 us (5120/1024 columns) and 8.48 -> 8.35 (8192/1024); at 4 per
+// SIMD 10.44 -> 11.67 (4096 tokens, 5120/1024) and 12.91 -> 14.49
+// (4096/4096), where the launch no longer fits one round.
+bool early_products(int64_t T, int num_cus, int dtype) {
+  return dtype == QKNORM_FP8_E4M3 && T <= int64_t{2} * 4 * num_cus;
+}
 void pair_rows(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
   v->pair = false;
   if (nseg != 2 || v->mode != qkn::MODE_FWD || v->nw != 4 || v->narrow || !v->nt || v->pipe ||
@@ -511,6 +521,7 @@ void pair_rows(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
   v->rpw = 1;
   v->pair = true;
   v->vpl_b = qkn::body_slots(v->vpl, a->seg[1].nslot);
+  v->early = early_products(a->T, ctx->num_cus, v->dtype);
 }
 
 // Packed rows: a launch over many rows (16 or more per SIMD, as for several

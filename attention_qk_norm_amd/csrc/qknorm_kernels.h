@@ -1181,7 +1181,7 @@ __device__ __forceinline__ void dispatch(const Hot& s, const Tables<VPL>& tb, in
 // tokens' rows have arrived (a barrier precedes its first store), where
 // separate wavefronts for the two segments let the narrow rows' stores start
 // while most rows are still being read.
-template <class E, int VA, int VB, int NW, bool NT>
+template <class E, int VA, int VB, int NW, bool NT, bool EARLY>
 __device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave, int lane, float* part,
                                           u32x4* lds_g) {
   const Layout<VA> La(wave, lane);
@@ -1206,13 +1206,17 @@ __device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave
   // its first store: the workgroup writes only after all its tokens' rows
   // have landed (the scheduling barrier keeps the compiler from moving the
   // narrow row's stores up between the statistics).
-  if constexpr (E::kSaturates) {
+  if constexpr (EARLY) {
     // FP8: the products x gamma are formed as the row vectors land, while
     // the statistics still wait for the rest, so after them only y = t r
     // and the encoding remain (one slice per row: the lane's squares in
     // slot order, then one wavefront sum each, as row_stat forms them).
-    // MI355X, gated back to back: C4-fp8 6.22 -> 6.05 us; the same for
-    // bf16 rows, whose scaling is lighter, took C4 8.48 -> 8.57 us.
+    // MI355X, gated back to back: C4-fp8 6.20 -> 5.99 us; the same for
+    // bf16 rows, whose scaling is lighter, took C4 8.48 -> 8.57 us. The
+    // products hold 16 VGPRs per slot, so these kernels keep 2 or 3
+    // wavefronts per SIMD, and the planner takes them for launches of at
+    // most 2 paired wavefronts per SIMD.
+    static_assert(E::kSaturates, "early products: FP8 rows");
     float ta[VA][E::kElems], tb[VB][E::kElems];
     float p[2] = {0.f, 0.f}, peak_a = 0.f, peak_b = 0.f;
 #pragma unroll
@@ -1244,7 +1248,7 @@ __device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave
 // wavefront needs from the kernel arguments is one round of scalar loads;
 // a paired launch reads both segments in that round.
 template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW = 1, int PAIRB = 0,
-          bool PACK = false>
+          bool PACK = false, bool EARLY = false>
 __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
   __shared__ float part[NW * kWave];  // per-wavefront slice partials (teams of > 1 wave)
   extern __shared__ u32x4 lds_g[];    // staged gamma (dynamic size: the launch's widest row)
@@ -1262,7 +1266,7 @@ __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
     Hot sa(a, a.seg[0]), sb(a, a.seg[1]);
     sa.paired_one_slice<VPL>();
     sb.paired_one_slice<PAIRB>();
-    body_pair<E, VPL, PAIRB, NW, NT>(sa, sb, wave, lane, part, lds_g);
+    body_pair<E, VPL, PAIRB, NW, NT, EARLY>(sa, sb, wave, lane, part, lds_g);
   } else {
     const Seg& seg = a.seg[blockIdx.y];
     const Hot s(a, seg);
@@ -1275,11 +1279,11 @@ __global__ void __launch_bounds__(NW * kWave) qknorm_kernel(const Args a) {
 // compiled() table names; any other combination instantiates nothing and is
 // refused.
 template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int RPW, int PAIRB = 0,
-          bool PACK = false>
+          bool PACK = false, bool EARLY = false>
 hipError_t launch_one(const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
-  if constexpr (compiled(E::kDtype, MODE, VPL, NW, NARROW, NT, PIPE, RPW, PAIRB, PACK)) {
-    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE, NARROW, NT, PIPE, RPW, PAIRB, PACK>), gd, dim3(NW * kWave),
-                       lds, st, a);
+  if constexpr (compiled(E::kDtype, MODE, VPL, NW, NARROW, NT, PIPE, RPW, PAIRB, PACK, EARLY)) {
+    hipLaunchKernelGGL((qknorm_kernel<E, VPL, NW, MODE, NARROW, NT, PIPE, RPW, PAIRB, PACK, EARLY>), gd,
+                       dim3(NW * kWave), lds, st, a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
@@ -1289,7 +1293,9 @@ hipError_t launch_one(const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
 // Paired launches: segment 1's body, down the chain VPL, VPL/2, ...
 template <class E, int VPL, int NW, int MODE, bool NARROW, bool NT, bool PIPE, int VB>
 hipError_t by_pair_b(const Variant& v, const Args& a, dim3 gd, unsigned lds, hipStream_t st) {
-  if (v.vpl_b == VB) return launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 1, VB>(a, gd, lds, st);
+  if (v.vpl_b == VB)
+    return v.early ? launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 1, VB, false, true>(a, gd, lds, st)
+                   : launch_one<E, VPL, NW, MODE, NARROW, NT, PIPE, 1, VB>(a, gd, lds, st);
   if constexpr (VB > 1) return by_pair_b<E, VPL, NW, MODE, NARROW, NT, PIPE, VB / 2>(v, a, gd, lds, st);
   return hipErrorInvalidValue;
 }

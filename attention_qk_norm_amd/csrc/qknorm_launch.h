@@ -174,6 +174,7 @@ struct Variant {
   int vpl_b = 0;      // paired: the body for segment 1's rows, on the chain vpl, vpl/2, ...
   bool pack = false;  // FWD, STATS, APPLY: rows of one slice and <= 32 vectors, several
                       // per slot (kPackSlots slots per wavefront)
+  bool early = false; // paired FP8: the products x gamma formed before the statistic
 };
 
 // Slots per wavefront of a packed launch; each holds 64 / 2^pack_log2 rows.
@@ -242,7 +243,8 @@ inline int compiled_vpl(int slots, int nw, int dtype) {
 //    wavefront, the second on the chain vpl, vpl/2, ...
 //  - packed rows (several narrow rows in each slot): forward, statistics and
 //    apply passes in 4-wavefront workgroups, streaming, one slot per row,
-//    kPackSlots slots per wavefront.
+//    kPackSlots slots per wavefront;
+//  - early products (x gamma formed before the statistic): paired FP8 rows.
 constexpr bool compiled_vpl_value(int vpl, int nw, int dtype) {
   if (vpl < 1 || vpl > max_slots(dtype, nw)) return false;
   if (nw == 4) {
@@ -255,8 +257,9 @@ constexpr bool compiled_vpl_value(int vpl, int nw, int dtype) {
   return false;
 }
 constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool nt, bool pipe, int rpw,
-                        int pair_b = 0, bool pack = false) {
+                        int pair_b = 0, bool pack = false, bool early = false) {
   if (!compiled_vpl_value(vpl, nw, dtype)) return false;
+  if (early && (dtype != QKNORM_FP8_E4M3 || pair_b == 0 || pack)) return false;
   if (pack)
     return (mode == MODE_FWD || mode == MODE_STATS || mode == MODE_APPLY) && vpl == 1 && nw == 4 && !narrow && nt &&
            !pipe && rpw == kPackSlots && pair_b == 0;
@@ -273,7 +276,8 @@ constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool 
   return true;
 }
 inline bool compiled(const Variant& v) {
-  return compiled(v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0, v.pack);
+  return compiled(v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0, v.pack,
+                  v.early);
 }
 
 // Enqueue one launch: grid.x workgroups per segment, grid.y segments, with

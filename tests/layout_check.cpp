@@ -43,9 +43,10 @@ static Variant g_v;
 static Args g_a;
 static dim3 g_grid;
 static unsigned g_lds;
-using VariantKey = std::tuple<int, int, int, int, bool, bool, bool, int, int, bool>;
+using VariantKey = std::tuple<int, int, int, int, bool, bool, bool, int, int, bool, bool>;
 static VariantKey key(const Variant& v) {
-  return VariantKey{v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0, v.pack};
+  return VariantKey{v.dtype, v.mode, v.vpl, v.nw, v.narrow, v.nt, v.pipe, v.rpw, v.pair ? v.vpl_b : 0, v.pack,
+                    v.early};
 }
 static long g_paired, g_packed, g_packed_covered;
 static void check_pair_launch(const Variant& v, const Args& a, dim3 grid, unsigned lds);
@@ -121,6 +122,9 @@ void qkn::check_pair_launch(const Variant& v, const Args& a, dim3 grid, unsigned
   }
   CHECK(s0.nslot >= s1.nslot && s0.nslot <= v.vpl && v.vpl_b == body_slots(v.vpl, s1.nslot),
         "paired slots %d/%d on bodies %d/%d", s0.nslot, s1.nslot, v.vpl, v.vpl_b);
+  // early products: FP8 launches of at most 2 paired wavefronts per SIMD (256 compute units)
+  CHECK(v.early == (v.dtype == QKNORM_FP8_E4M3 && a.T <= 2 * 4 * 256), "paired T=%lld early=%d",
+        (long long)a.T, v.early ? 1 : 0);
   CHECK(s0.nwg == s1.nwg && int64_t{s0.nwg} * 4 >= a.T && int64_t{s0.nwg - 1} * 4 < a.T && grid.x == unsigned(s0.nwg) &&
             grid.y == 1,
         "paired grid %u x %u for %d workgroups", grid.x, grid.y, s0.nwg);
@@ -437,8 +441,8 @@ static void print_plan(const char* name, int dtype, int64_t T, int64_t hq, int64
   pair_rows(&ctx, &v, &a, 2);
   if (!v.pair) pack_rows(&ctx, &v, &a, 2);
   if (!v.pair && !v.pack) rows_per_wave(&ctx, &v, &a, 2);
-  std::printf("plan %s: nw=%d body=%d narrow=%d rows_per_wave=%d paired=%d", name, nw, v.vpl, narrow ? 1 : 0, v.rpw,
-              v.pair ? v.vpl_b : 0);
+  std::printf("plan %s: nw=%d body=%d narrow=%d rows_per_wave=%d paired=%d early=%d", name, nw, v.vpl,
+              narrow ? 1 : 0, v.rpw, v.pair ? v.vpl_b : 0, v.early ? 1 : 0);
   for (int i = 0; i < 2; ++i)
     std::printf(" | %s team=%d sub_lanes=%d slots=%d masked=%d", i ? "k" : "q", 1 << plans[i].wpr_log2,
                 1 << plans[i].sub_lanes_log2, plans[i].slots, plans[i].masked ? 1 : 0);
@@ -461,7 +465,7 @@ static long sweep_entry_points() {
   std::vector<int64_t> widths = {8, 64, 200, 1000, 1280, 12288, 24576, 49152, 65536};
   for (int64_t slots = 1; slots <= 32; ++slots)
     for (int64_t per : {256, 512, 1024}) widths.push_back(slots * per);
-  const int64_t rows[] = {1, 64, 256, 2048, 16384, 100000};
+  const int64_t rows[] = {1, 64, 256, 2048, 3001, 16384, 100000};
   const int ks[] = {1, 2, 4, 8, 64};
   for (const qknorm_options& o : opts) {
     qknorm_ctx ctx{0, 256, o};
@@ -563,22 +567,26 @@ int main() {
               for (int pipe = 0; pipe < 2; ++pipe)
                 for (int rpw : {1, 2, 4})
                   for (int pb = 0; pb <= qkn::kMaxSlots; ++pb)
-                    for (int pk = 0; pk < 2; ++pk) {
-                      if (!qkn::compiled(dtype, mode, vpl, nw, narrow, nt, pipe, rpw, pb, pk != 0)) continue;
-                      ++compiled_n;
-                      const qkn::VariantKey k{dtype, mode, vpl, nw, narrow != 0, nt != 0, pipe != 0, rpw, pb,
-                                              pk != 0};
-                      if (!qkn::g_reached.count(k)) unused.push_back(k);
-                    }
+                    for (int pk = 0; pk < 2; ++pk)
+                      for (int ea = 0; ea < 2; ++ea) {
+                        if (!qkn::compiled(dtype, mode, vpl, nw, narrow, nt, pipe, rpw, pb, pk != 0, ea != 0))
+                          continue;
+                        ++compiled_n;
+                        const qkn::VariantKey k{dtype, mode, vpl, nw, narrow != 0, nt != 0, pipe != 0, rpw, pb,
+                                                pk != 0, ea != 0};
+                        if (!qkn::g_reached.count(k)) unused.push_back(k);
+                      }
   std::printf("entry points: %ld calls, %ld launches, %zu variants reached, %ld compiled, %zu compiled and "
               "never reached\n", calls, qkn::g_launches, qkn::g_reached.size(), compiled_n, unused.size());
   std::printf("paired launches %ld; packed launches %ld, %ld segments traced lane by lane\n", qkn::g_paired,
               qkn::g_packed, qkn::g_packed_covered);
   CHECK(unused.empty(), "%zu compiled variants that no call reaches", unused.size());
   for (const auto& k : unused)
-    std::printf("  unreached: dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d paired=%d packed=%d\n",
+    std::printf("  unreached: dtype=%d mode=%d vpl=%d nw=%d narrow=%d nt=%d pipe=%d rpw=%d paired=%d packed=%d "
+                "early=%d\n",
                 std::get<0>(k), std::get<1>(k), std::get<2>(k), std::get<3>(k), (int)std::get<4>(k),
-                (int)std::get<5>(k), (int)std::get<6>(k), std::get<7>(k), std::get<8>(k), (int)std::get<9>(k));
+                (int)std::get<5>(k), (int)std::get<6>(k), std::get<7>(k), std::get<8>(k), (int)std::get<9>(k),
+                (int)std::get<10>(k));
   std::printf("%d cases, %d failures\n", cases, failures);
   return failures ? 1 : 0;
 }

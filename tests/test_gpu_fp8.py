@@ -257,12 +257,14 @@ def test_fp8_dense_saturation(in_place, K, opts):
     (3001, 1024, 4096, "in_place"),     # key rows wider (the segments swap), T not a multiple of 4
     (2048, 4096, 4096, "plain"),
     (2560, 5120, 1024, "saturating"),   # weights of +-(200..600), a NaN and a zero row, in place
+    (2048, 5120, 1024, "saturating"),   # the same with the products formed before the statistic
 ])
 def test_fp8_paired_rows(T, Hq, Hk, case):
     """FP8 forward launches of 2 to 4 paired wavefronts per SIMD (each
-    wavefront takes one token's query and key row): parity, and bit equality
-    with the same launch unpaired (a forced team of one wavefront), also when
-    rows saturate and are encoded again with the clamp from the input."""
+    wavefront takes one token's query and key row; at 2 per SIMD the kernel
+    forms the products x gamma before the statistic): parity, and bit
+    equality with the same launch unpaired (a forced team of one wavefront),
+    also when rows saturate and are encoded again with the clamp."""
     q = rows(T, Hq, [61, T], dist="laplace")
     k = rows(T, Hk, [62, T])
     gq, gk = weights(Hq, 63), weights(Hk, 64)

@@ -16,17 +16,17 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # team = wavefronts per row, sub_lanes = lanes that deal one slice, slots =
 # 16-byte vectors per lane, body = the compiled slot count the launch runs
 WORKLOAD_PLANS = [
-    'plan c1 K=1: nw=4 body=1 narrow=0 rows_per_wave=1 paired=0 | q team=4 sub_lanes=64 slots=1 masked=0 | k team=4 sub_lanes=64 slots=1 masked=0',
-    'plan c1 K=4: nw=4 body=1 narrow=0 rows_per_wave=1 paired=0 | q team=4 sub_lanes=64 slots=1 masked=0 | k team=4 sub_lanes=64 slots=1 masked=0',
-    'plan c2 K=1: nw=4 body=2 narrow=0 rows_per_wave=1 paired=0 | q team=4 sub_lanes=256 slots=2 masked=0 | k team=4 sub_lanes=256 slots=2 masked=0',
-    'plan c3 K=4: nw=4 body=3 narrow=0 rows_per_wave=1 paired=0 | q team=4 sub_lanes=64 slots=3 masked=0 | k team=4 sub_lanes=64 slots=3 masked=0',
-    'plan c3 K=1: nw=4 body=3 narrow=0 rows_per_wave=1 paired=0 | q team=4 sub_lanes=256 slots=3 masked=0 | k team=4 sub_lanes=256 slots=3 masked=0',
-    'plan c4 K=1: nw=4 body=10 narrow=0 rows_per_wave=1 paired=2 | q team=1 sub_lanes=64 slots=10 masked=0 | k team=1 sub_lanes=64 slots=2 masked=0',
-    'plan c5 K=8: nw=4 body=4 narrow=0 rows_per_wave=1 paired=0 | q team=2 sub_lanes=64 slots=4 masked=0 | k team=2 sub_lanes=64 slots=4 masked=0',
-    'plan c5 K=1: nw=4 body=4 narrow=0 rows_per_wave=1 paired=0 | q team=2 sub_lanes=128 slots=4 masked=0 | k team=2 sub_lanes=128 slots=4 masked=0',
-    'plan c4f8 K=1: nw=4 body=5 narrow=0 rows_per_wave=1 paired=1 | q team=1 sub_lanes=64 slots=5 masked=0 | k team=1 sub_lanes=64 slots=1 masked=0',
-    'plan c5f8 K=8: nw=4 body=4 narrow=1 rows_per_wave=1 paired=0 | q team=1 sub_lanes=8 slots=4 masked=0 | k team=1 sub_lanes=8 slots=4 masked=0',
-    'plan c5f8 K=1: nw=4 body=4 narrow=0 rows_per_wave=1 paired=0 | q team=1 sub_lanes=64 slots=4 masked=0 | k team=1 sub_lanes=64 slots=4 masked=0',
+    'plan c1 K=1: nw=4 body=1 narrow=0 rows_per_wave=1 paired=0 early=0 | q team=4 sub_lanes=64 slots=1 masked=0 | k team=4 sub_lanes=64 slots=1 masked=0',
+    'plan c1 K=4: nw=4 body=1 narrow=0 rows_per_wave=1 paired=0 early=0 | q team=4 sub_lanes=64 slots=1 masked=0 | k team=4 sub_lanes=64 slots=1 masked=0',
+    'plan c2 K=1: nw=4 body=2 narrow=0 rows_per_wave=1 paired=0 early=0 | q team=4 sub_lanes=256 slots=2 masked=0 | k team=4 sub_lanes=256 slots=2 masked=0',
+    'plan c3 K=4: nw=4 body=3 narrow=0 rows_per_wave=1 paired=0 early=0 | q team=4 sub_lanes=64 slots=3 masked=0 | k team=4 sub_lanes=64 slots=3 masked=0',
+    'plan c3 K=1: nw=4 body=3 narrow=0 rows_per_wave=1 paired=0 early=0 | q team=4 sub_lanes=256 slots=3 masked=0 | k team=4 sub_lanes=256 slots=3 masked=0',
+    'plan c4 K=1: nw=4 body=10 narrow=0 rows_per_wave=1 paired=2 early=0 | q team=1 sub_lanes=64 slots=10 masked=0 | k team=1 sub_lanes=64 slots=2 masked=0',
+    'plan c5 K=8: nw=4 body=4 narrow=0 rows_per_wave=1 paired=0 early=0 | q team=2 sub_lanes=64 slots=4 masked=0 | k team=2 sub_lanes=64 slots=4 masked=0',
+    'plan c5 K=1: nw=4 body=4 narrow=0 rows_per_wave=1 paired=0 early=0 | q team=2 sub_lanes=128 slots=4 masked=0 | k team=2 sub_lanes=128 slots=4 masked=0',
+    'plan c4f8 K=1: nw=4 body=5 narrow=0 rows_per_wave=1 paired=1 early=1 | q team=1 sub_lanes=64 slots=5 masked=0 | k team=1 sub_lanes=64 slots=1 masked=0',
+    'plan c5f8 K=8: nw=4 body=4 narrow=1 rows_per_wave=1 paired=0 early=0 | q team=1 sub_lanes=8 slots=4 masked=0 | k team=1 sub_lanes=8 slots=4 masked=0',
+    'plan c5f8 K=1: nw=4 body=4 narrow=0 rows_per_wave=1 paired=0 early=0 | q team=1 sub_lanes=64 slots=4 masked=0 | k team=1 sub_lanes=64 slots=4 masked=0',
 ]
 
 
