@@ -521,7 +521,7 @@ void pair_rows(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
   v->rpw = 1;
   v->pair = true;
   v->vpl_b = qkn::body_slots(v->vpl, a->seg[1].nslot);
-  v->early = early_products(a->T, ctx->num_cus, v->dtype);
+  v->early = early_products(a->T, ctx->num_cus, v->dtype) && v->vpl + v->vpl_b <= qkn::kEarlySlots;
 }
 
 // Packed rows: a launch over many rows (16 or more per SIMD, as for several

@@ -1214,8 +1214,9 @@ __device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave
     // MI355X, gated back to back: C4-fp8 6.20 -> 5.99 us; the same for
     // bf16 rows, whose scaling is lighter, took C4 8.48 -> 8.57 us. The
     // products hold 16 VGPRs per slot, so these kernels keep 2 or 3
-    // wavefronts per SIMD, and the planner takes them for launches of at
-    // most 2 paired wavefronts per SIMD.
+    // wavefronts per SIMD; they are built for rows of at most kEarlySlots
+    // slots together, and the planner takes them for launches of at most 2
+    // paired wavefronts per SIMD.
     static_assert(E::kSaturates, "early products: FP8 rows");
     float ta[VA][E::kElems], tb[VB][E::kElems];
     float p[2] = {0.f, 0.f}, peak_a = 0.f, peak_b = 0.f;

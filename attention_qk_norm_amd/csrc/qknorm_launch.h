@@ -177,6 +177,12 @@ struct Variant {
   bool early = false; // paired FP8: the products x gamma formed before the statistic
 };
 
+// Paired FP8 rows form the products x gamma early only when the two rows
+// hold at most kEarlySlots slots together: the products take 16 VGPRs per
+// slot, and wider pairs would need more than 256 registers (one wavefront
+// per SIMD).
+constexpr int kEarlySlots = 12;
+
 // Slots per wavefront of a packed launch; each holds 64 / 2^pack_log2 rows.
 constexpr int kPackSlots = 4;
 
@@ -259,7 +265,7 @@ constexpr bool compiled_vpl_value(int vpl, int nw, int dtype) {
 constexpr bool compiled(int dtype, int mode, int vpl, int nw, bool narrow, bool nt, bool pipe, int rpw,
                         int pair_b = 0, bool pack = false, bool early = false) {
   if (!compiled_vpl_value(vpl, nw, dtype)) return false;
-  if (early && (dtype != QKNORM_FP8_E4M3 || pair_b == 0 || pack)) return false;
+  if (early && (dtype != QKNORM_FP8_E4M3 || pair_b == 0 || pack || vpl + pair_b > kEarlySlots)) return false;
   if (pack)
     return (mode == MODE_FWD || mode == MODE_STATS || mode == MODE_APPLY) && vpl == 1 && nw == 4 && !narrow && nt &&
            !pipe && rpw == kPackSlots && pair_b == 0;

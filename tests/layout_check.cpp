@@ -123,8 +123,8 @@ void qkn::check_pair_launch(const Variant& v, const Args& a, dim3 grid, unsigned
   CHECK(s0.nslot >= s1.nslot && s0.nslot <= v.vpl && v.vpl_b == body_slots(v.vpl, s1.nslot),
         "paired slots %d/%d on bodies %d/%d", s0.nslot, s1.nslot, v.vpl, v.vpl_b);
   // early products: FP8 launches of at most 2 paired wavefronts per SIMD (256 compute units)
-  CHECK(v.early == (v.dtype == QKNORM_FP8_E4M3 && a.T <= 2 * 4 * 256), "paired T=%lld early=%d",
-        (long long)a.T, v.early ? 1 : 0);
+  CHECK(v.early == (v.dtype == QKNORM_FP8_E4M3 && a.T <= 2 * 4 * 256 && v.vpl + v.vpl_b <= kEarlySlots),
+        "paired T=%lld slots %d + %d early=%d", (long long)a.T, v.vpl, v.vpl_b, v.early ? 1 : 0);
   CHECK(s0.nwg == s1.nwg && int64_t{s0.nwg} * 4 >= a.T && int64_t{s0.nwg - 1} * 4 < a.T && grid.x == unsigned(s0.nwg) &&
             grid.y == 1,
         "paired grid %u x %u for %d workgroups", grid.x, grid.y, s0.nwg);
