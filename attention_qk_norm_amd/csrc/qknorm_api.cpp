@@ -447,7 +447,7 @@ void share_gamma(qkn::Seg* s, int dtype) {
 //    those keep one row per wavefront.
 //
 // (FP8 forward launches of a single round once took 2 rows of one tensor per
-// wavefront: C4-fp8 8.0 -> 7.15 us at the time. Paired rows serve those
+// wavefront: 2048 x 5120/1024 FP8 8.0 -> 7.15 us at the time. Paired rows serve those
 // launches better, 6.45 -> 6.34 us, and below 2 paired wavefronts per SIMD one
 // row per wavefront is best: 1024 x 5120/1024 4.46 us against 5.57 with two.)
 void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nseg) {
@@ -482,10 +482,10 @@ void rows_per_wave(const qknorm_ctx* ctx, qkn::Variant* v, qkn::Args* a, int nse
 // being read; reads and writes mixed in HBM cost more than either alone (24
 // MiB each way: 4.99 us read only, 4.78 us write only, 9.87 us as one
 // copy). MI355X, gated back to back, bit for bit the unpaired results,
-// against the same launch unpaired: C4 (2048 x 5120/1024 bf16) 9.77 -> 8.68
-// us; 1792 x 4096/4096 12.49 -> 10.55; 4096 x 2048/512 9.05 -> 8.42; fp32
-// 2048 x 2048/512 8.89 -> 7.40; FP8 3072 x 5120/1024 8.98 -> 8.32, C4-fp8
-// 6.45 (two rows of one tensor per wavefront) -> 6.34. From about five per
+// against the same launch unpaired: 2048 x 5120/1024 bf16 9.77 -> 8.68 us;
+// 1792 x 4096/4096 12.49 -> 10.55; 4096 x 2048/512 9.05 -> 8.42; fp32 2048 x
+// 2048/512 8.89 -> 7.40; FP8 3072 x 5120/1024 8.98 -> 8.32, FP8 2048 x
+// 5120/1024 6.45 (two rows of one tensor per wavefront) -> 6.34. From about five per
 // SIMD the other wavefronts already overlap each row's chain and pairing
 // mostly loses (8192 x 4096/1024: 28.5 -> 29.4; FP8 6144 x 5120/1024: 15.1
 // -> 16.7); FP8 rows below two per SIMD run best unpaired (1536 x
