@@ -725,10 +725,10 @@ __device__ __forceinline__ void scale_store(const u32x4 (&d)[VPL], const typenam
 
 // FP8 rows whose products x gamma (E::products) were formed while the row's
 // statistic was pending: y = t r, encoded as encode_store does. `peak` is
-// the lane's largest |t|; when peak * r passes 448 the lane
-// encodes all its vectors with the clamp (the same bits as encode_store's
-// redo, which clamps only the vectors past the range: the clamp leaves the
-// others as they are).
+// the lane's largest |t|; when peak * r passes 448 the lane encodes all its
+// vectors with the clamp (the same bits as encode_store's redo, which
+// clamps only the vectors past the range: the clamp leaves the others as
+// they are).
 template <class E, int VPL, bool NT>
 __device__ __forceinline__ void products_store(const float (&t)[VPL][E::kElems], float peak, float S,
                                                const Hot& s, int64_t row, bool live, const Layout<VPL>& L) {
@@ -1213,11 +1213,10 @@ __device__ __forceinline__ void body_pair(const Hot& sa, const Hot& sb, int wave
     // slot order, then one wavefront sum each, as row_stat forms them).
     // MI355X, gated back to back, 2048 tokens of 5120/1024 columns: FP8
     // 6.20 -> 5.99 us; the same for bf16 rows, whose scaling is lighter,
-    // 8.48 -> 8.57 us. The
-    // products hold 16 VGPRs per slot, so these kernels keep 2 or 3
-    // wavefronts per SIMD; they are built for rows of at most kEarlySlots
-    // slots together, and the planner takes them for launches of at most 2
-    // paired wavefronts per SIMD.
+    // 8.48 -> 8.57 us. The products hold 16 VGPRs per slot, so these
+    // kernels keep 2 or 3 wavefronts per SIMD; they are built for rows of at
+    // most kEarlySlots slots together, and the planner takes them for
+    // launches of at most 2 paired wavefronts per SIMD.
     static_assert(E::kSaturates, "early products: FP8 rows");
     float ta[VA][E::kElems], tb[VB][E::kElems];
     float p[2] = {0.f, 0.f}, peak_a = 0.f, peak_b = 0.f;
