@@ -258,6 +258,8 @@ def test_fp8_dense_saturation(in_place, K, opts):
     (2048, 4096, 4096, "plain"),
     (2560, 5120, 1024, "saturating"),   # weights of +-(200..600), a NaN and a zero row, in place
     (2048, 5120, 1024, "saturating"),   # the same with the products formed before the statistic
+    (2048, 6144, 6144, "plain"),        # 6 + 6 slots: the widest pair with early products
+    (2048, 7168, 7168, "plain"),        # 7 + 7 slots: scaled after the statistic
 ])
 def test_fp8_paired_rows(T, Hq, Hk, case):
     """FP8 forward launches of 2 to 4 paired wavefronts per SIMD (each
